@@ -1,0 +1,164 @@
+"""CPU oracle for the fused SwiGLU MLP (test infrastructure only).
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package.  The GPU library never calls it, and it calls nothing of the
+GPU library: the two share no code.
+
+`oracle.c` holds the arithmetic (fp64, plain loops); this module only loads
+it with ctypes and marshals NumPy arrays.  `brute.py` is a second, pure-Python
+implementation for tiny shapes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc build of an oracle source: IEEE fp64, no FMA contraction, OpenMP
+    over independent output elements."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fopenmp", "-fPIC", "-shared", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (when missing or stale)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+def _bind(lib):
+    i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+    lib.oracle_bf16_to_double.restype = ctypes.c_double
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_sigmoid.restype = ctypes.c_double
+    lib.oracle_sigmoid.argtypes = [ctypes.c_double]
+    lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_swiglu_rows.restype = ctypes.c_int
+    lib.oracle_swiglu_rows.argtypes = [ctypes.c_int, vp, vp, vp, i64, i64, i64,
+                                       vp, i64, dp, dp, dp, ctypes.c_int]
+    lib.oracle_mlp_rows.restype = ctypes.c_int
+    lib.oracle_mlp_rows.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64,
+                                    vp, i64, dp, dp, ctypes.c_int]
+    lib.oracle_default_threads.restype = ctypes.c_int
+    lib.oracle_default_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = _bind(ctypes.CDLL(build()))
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_of(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle inputs are float32 arrays or uint16 bf16 bit patterns")
+
+
+def _check(x, wg, wu, wd=None):
+    dt = _dtype_of(x)
+    for w in (wg, wu) + ((wd,) if wd is not None else ()):
+        if _dtype_of(w) != dt:
+            raise TypeError("x and the weights must share one dtype")
+    M, d = x.shape
+    d2, dff = wg.shape
+    if d2 != d or wu.shape != (d, dff) or (wd is not None and wd.shape != (dff, d)):
+        raise ValueError("shape mismatch")
+    return dt, M, d, dff
+
+
+def _rows_arg(rows, M):
+    if rows is None:
+        return None, M
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, len(r)
+
+
+def bf16_to_double(bits: int, lib=None) -> float:
+    return (lib or _load()).oracle_bf16_to_double(bits)
+
+
+def sigmoid(z: float, lib=None) -> float:
+    return (lib or _load()).oracle_sigmoid(float(z))
+
+
+def silu(z: float, lib=None) -> float:
+    return (lib or _load()).oracle_silu(float(z))
+
+
+def swiglu(x, wg, wu, rows=None, want_gu=False, nthreads=0, lib=None):
+    """h = silu(x.Wg) * (x.Wu) in fp64 for the given rows of x (all rows if
+    None).  With want_gu, also returns g and u."""
+    x, wg, wu = (np.ascontiguousarray(a) for a in (x, wg, wu))
+    dt, M, d, dff = _check(x, wg, wu)
+    r, nrows = _rows_arg(rows, M)
+    h = np.empty((nrows, dff), dtype=np.float64)
+    g = np.empty_like(h) if want_gu else None
+    u = np.empty_like(h) if want_gu else None
+    rc = (lib or _load()).oracle_swiglu_rows(dt, _ptr(x), _ptr(wg), _ptr(wu), M, d, dff,
+                                    _ptr(r), nrows, _ptr(g), _ptr(u), _ptr(h), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_swiglu_rows failed (%d)" % rc)
+    return (h, g, u) if want_gu else h
+
+
+def mlp(x, wg, wu, wd, rows=None, want_h=False, nthreads=0, lib=None):
+    """y = (silu(x.Wg) * (x.Wu)) . Wd in fp64 for the given rows of x."""
+    x, wg, wu, wd = (np.ascontiguousarray(a) for a in (x, wg, wu, wd))
+    dt, M, d, dff = _check(x, wg, wu, wd)
+    r, nrows = _rows_arg(rows, M)
+    y = np.empty((nrows, d), dtype=np.float64)
+    h = np.empty((nrows, dff), dtype=np.float64) if want_h else None
+    rc = (lib or _load()).oracle_mlp_rows(dt, _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), M, d, dff,
+                                 _ptr(r), nrows, _ptr(h), _ptr(y), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_mlp_rows failed (%d)" % rc)
+    return (y, h) if want_h else y
+
+
+def default_threads() -> int:
+    return _load().oracle_default_threads()
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def load_library(path: str):
+    """Bind another build of oracle.c (used by the tests that plant
+    mistakes in a copy of the source); pass the handle as `lib=`."""
+    return _bind(ctypes.CDLL(path))
+
+
+def available_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1

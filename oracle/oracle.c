@@ -1,0 +1,197 @@
+/*
+ * oracle.c -- plain CPU reference for the fused SwiGLU MLP.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code with the GPU
+ * library and is never used to produce a product result.
+ *
+ * What it computes (fp64 throughout, no blocking of the sums):
+ *   g = x . Wgate,  u = x . Wup                  (two independent products;
+ *       Tile-Level Activation Overlap for Efficient LLM Inference, problem
+ *       statement: Y = SiLU(A x W1) (.) (A x W2))
+ *   h = silu(g) * u,  silu(z) = z * sigmoid(z)   (same passage; SiLU is the
+ *       Swish activation with beta = 1)
+ *   y = h . Wdown                                (optional down projection;
+ *       "Anatomie d'un transformeur sur GPU" §1.1 layer skeleton, and the
+ *       §1.2 projection table: Wgate and Wup are d x d_ff, Wdown is d_ff x d)
+ *
+ * Inputs are the exact bits handed to the GPU: fp32 arrays, or bf16 stored
+ * as raw uint16 patterns, which are widened exactly (bits << 16 -> float ->
+ * double).  Every element of g, u and y is a sum taken in ascending order of
+ * the contraction index.  Threads only split independent output elements,
+ * so results do not depend on the thread count.  h is never rounded before
+ * the down projection.
+ *
+ * Layouts: x is M x d, Wgate and Wup are d x dff, Wdown is dff x d, all
+ * row-major.  Parity pins: tests/test_oracle.py (closed forms, integer-exact
+ * products, one-hot rows, brute force on tiny shapes).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* bf16 is the top 16 bits of an IEEE binary32; widening is exact. */
+double oracle_bf16_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static inline double elem(const void *p, int dtype, int64_t i)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)p)[i];
+    return oracle_bf16_to_double(((const uint16_t *)p)[i]);
+}
+
+/* Logistic function 1/(1+e^-z), written so that exp never overflows. */
+double oracle_sigmoid(double z)
+{
+    if (z >= 0.0)
+        return 1.0 / (1.0 + exp(-z));
+    double e = exp(z);
+    return e / (1.0 + e);
+}
+
+/* SiLU (Swish with beta = 1): z * sigmoid(z). */
+double oracle_silu(double z)
+{
+    return z * oracle_sigmoid(z);
+}
+
+static int bad_dims(int dtype, int64_t M, int64_t d, int64_t dff)
+{
+    return (dtype != ORACLE_F32 && dtype != ORACLE_BF16) || M < 0 || d <= 0 || dff <= 0;
+}
+
+static int threads_or_default(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Columns handled by one task: independent output elements only. */
+#define COL_BLOCK 512
+
+/*
+ * Gate and up products for the selected rows of x.
+ *   rows: indices into x (nrows of them), or NULL for rows 0..nrows-1.
+ *   g, u, h: nrows x dff outputs (each may be NULL if not wanted).
+ * h[r][n] = silu(g[r][n]) * u[r][n].  Returns 0, or -1 on bad arguments.
+ */
+int oracle_swiglu_rows(int dtype, const void *x, const void *wg, const void *wu,
+                       int64_t M, int64_t d, int64_t dff,
+                       const int64_t *rows, int64_t nrows,
+                       double *g, double *u, double *h, int nthreads)
+{
+    if (bad_dims(dtype, M, d, dff) || nrows < 0 || !x || !wg || !wu)
+        return -1;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t m = rows ? rows[r] : r;
+        if (m < 0 || m >= M)
+            return -1;
+    }
+    int64_t nblocks = (dff + COL_BLOCK - 1) / COL_BLOCK;
+    int nt = threads_or_default(nthreads);
+    int err = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) collapse(2)
+    for (int64_t r = 0; r < nrows; ++r) {
+        for (int64_t b = 0; b < nblocks; ++b) {
+            int64_t m = rows ? rows[r] : r;
+            int64_t n0 = b * COL_BLOCK;
+            int64_t n1 = n0 + COL_BLOCK < dff ? n0 + COL_BLOCK : dff;
+            double *gs = (double *)calloc((size_t)(n1 - n0), sizeof(double));
+            double *us = (double *)calloc((size_t)(n1 - n0), sizeof(double));
+            if (!gs || !us) {
+                free(gs);
+                free(us);
+#pragma omp atomic write
+                err = 1;
+                continue;
+            }
+            /* g[n] = sum_k x[m][k] * Wg[k][n], k ascending; likewise u. */
+            for (int64_t k = 0; k < d; ++k) {
+                double xv = elem(x, dtype, m * d + k);
+                for (int64_t n = n0; n < n1; ++n) {
+                    gs[n - n0] += xv * elem(wg, dtype, k * dff + n);
+                    us[n - n0] += xv * elem(wu, dtype, k * dff + n);
+                }
+            }
+            for (int64_t n = n0; n < n1; ++n) {
+                double gv = gs[n - n0], uv = us[n - n0];
+                if (g)
+                    g[r * dff + n] = gv;
+                if (u)
+                    u[r * dff + n] = uv;
+                if (h)
+                    h[r * dff + n] = oracle_silu(gv) * uv;
+            }
+            free(gs);
+            free(us);
+        }
+    }
+    return err ? -1 : 0;
+}
+
+/*
+ * Full MLP for the selected rows: y[r][j] = sum_n h[r][n] * Wd[n][j], with h
+ * from oracle_swiglu_rows, unrounded, and n ascending.
+ *   h_out (nrows x dff) may be NULL; y (nrows x d) is required.
+ */
+int oracle_mlp_rows(int dtype, const void *x, const void *wg, const void *wu,
+                    const void *wd, int64_t M, int64_t d, int64_t dff,
+                    const int64_t *rows, int64_t nrows,
+                    double *h_out, double *y, int nthreads)
+{
+    if (bad_dims(dtype, M, d, dff) || nrows < 0 || !wd || !y)
+        return -1;
+    double *h = h_out;
+    if (!h) {
+        h = (double *)malloc((size_t)(nrows > 0 ? nrows : 1) * (size_t)dff * sizeof(double));
+        if (!h)
+            return -1;
+    }
+    int rc = oracle_swiglu_rows(dtype, x, wg, wu, M, d, dff, rows, nrows,
+                                NULL, NULL, h, nthreads);
+    if (rc == 0) {
+        int64_t nblocks = (d + COL_BLOCK - 1) / COL_BLOCK;
+        int nt = threads_or_default(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt) collapse(2)
+        for (int64_t r = 0; r < nrows; ++r) {
+            for (int64_t b = 0; b < nblocks; ++b) {
+                int64_t j0 = b * COL_BLOCK;
+                int64_t j1 = j0 + COL_BLOCK < d ? j0 + COL_BLOCK : d;
+                for (int64_t j = j0; j < j1; ++j)
+                    y[r * d + j] = 0.0;
+                for (int64_t n = 0; n < dff; ++n) {
+                    double hv = h[r * dff + n];
+                    for (int64_t j = j0; j < j1; ++j)
+                        y[r * d + j] += hv * elem(wd, dtype, n * d + j);
+                }
+            }
+        }
+    }
+    if (!h_out)
+        free(h);
+    return rc;
+}
+
+/* Number of threads an nthreads=0 call would use (for reporting). */
+int oracle_default_threads(void)
+{
+    return threads_or_default(0);
+}

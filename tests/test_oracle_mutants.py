@@ -1,0 +1,91 @@
+"""Plant typical mistakes in copies of the oracle's C source (on the CPU)
+and check that the pins reject every one of them, while accepting the real
+oracle.  This shows the pins are sharp enough to catch a dropped term, a
+wrong sign, a transposed operand, a wrong index or a swapped pairing."""
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import workloads as wl
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "sigmoid_sign": ("return z * oracle_sigmoid(z);", "return z * oracle_sigmoid(-z);"),
+    "swapped_pairing": ("h[r * dff + n] = oracle_silu(gv) * uv;",
+                        "h[r * dff + n] = oracle_silu(uv) * gv;"),
+    "dropped_first_term": ("for (int64_t k = 0; k < d; ++k) {",
+                           "for (int64_t k = 1; k < d; ++k) {"),
+    "transposed_gate": ("gs[n - n0] += xv * elem(wg, dtype, k * dff + n);",
+                        "gs[n - n0] += xv * elem(wg, dtype, n * d + k);"),
+    "transposed_x": ("double xv = elem(x, dtype, m * d + k);",
+                     "double xv = elem(x, dtype, k * M + m);"),
+    "transposed_down": ("y[r * d + j] += hv * elem(wd, dtype, n * d + j);",
+                        "y[r * d + j] += hv * elem(wd, dtype, j * dff + n);"),
+    "bf16_shift": ("uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+    "up_uses_gate": ("us[n - n0] += xv * elem(wu, dtype, k * dff + n);",
+                     "us[n - n0] += xv * elem(wg, dtype, k * dff + n);"),
+    "dropped_last_down_term": ("for (int64_t n = 0; n < dff; ++n) {\n                    double hv",
+                               "for (int64_t n = 0; n < dff - 1; ++n) {\n                    double hv"),
+}
+
+
+def _dec(a):
+    return a.astype(np.float64) if a.dtype == np.float32 else wl.bf16_bits_to_f32(a).astype(np.float64)
+
+
+def pin_failures(lib):
+    """Run a compact set of the pins against `lib`; return the failed ones."""
+    failed = []
+
+    def check(name, fn):
+        try:
+            if not fn():
+                failed.append(name)
+        except Exception:  # a crash or a raised error counts as a failure
+            failed.append(name)
+
+    check("bf16", lambda: oracle.bf16_to_double(0x4049, lib=lib) == 3.140625)
+    check("silu_log3", lambda: abs(oracle.silu(np.log(3.0), lib=lib) - np.log(3.0) * 0.75) < 1e-15)
+    for dtype in (wl.F32, wl.BF16):
+        inp = wl.integer_inputs(5, 3, 37, 29, dtype, with_down=True, lo=-3, hi=3)
+        xi = _dec(inp["x"]).astype(np.int64)
+        gi = (xi @ _dec(inp["wg"]).astype(np.int64)).astype(np.float64)
+        ui = (xi @ _dec(inp["wu"]).astype(np.int64)).astype(np.float64)
+        href = gi * scipy.special.expit(gi) * ui
+        yref = href @ _dec(inp["wd"])
+
+        def prod():
+            _, g, u = oracle.swiglu(inp["x"], inp["wg"], inp["wu"], want_gu=True, lib=lib)
+            return np.array_equal(g, gi) and np.array_equal(u, ui)
+
+        def act():
+            h = oracle.swiglu(inp["x"], inp["wg"], inp["wu"], lib=lib)
+            return np.allclose(h, href, rtol=1e-14, atol=0)
+
+        def down():
+            y = oracle.mlp(inp["x"], inp["wg"], inp["wu"], inp["wd"], lib=lib)
+            return np.allclose(y, yref, rtol=1e-12, atol=1e-12)
+
+        check("products_%d" % dtype, prod)
+        check("activation_%d" % dtype, act)
+        check("down_%d" % dtype, down)
+    return failed
+
+
+def test_real_oracle_passes_compact_pins():
+    assert pin_failures(None) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) == 1, "mutation anchor not found: " + name
+    mut = tmp_path / ("oracle_%s.c" % name)
+    mut.write_text(src.replace(before, after))
+    lib = oracle.load_library(oracle.compile_source(str(mut), str(tmp_path / ("lib%s.so" % name))))
+    assert pin_failures(lib), "planted mistake %s went unnoticed" % name
