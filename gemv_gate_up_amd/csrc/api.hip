@@ -1,0 +1,317 @@
+// api.hip -- the exported C ABI: argument checks, the M-based dispatcher,
+// workspace layout and the launches of the hot path.
+//
+// Dispatcher: few rows go to the split-over-weights kernels (the narrow-
+// matrix kernel of "Où part le temps d'un token" serves any product whose
+// left operand has at most 16 rows; ours extends it to 64 rows by giving
+// each wave up to four 16-row MFMA tiles); more rows go to the fused MFMA
+// GEMM ("Tile-Level Activation Overlap for Efficient LLM Inference" picks
+// between its two kernels by batch size in the same way).
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.h"
+#include "swiglu.h"
+
+namespace swg {
+namespace {
+
+constexpr int64_t MAX_DIM = (int64_t)1 << 20;
+constexpr int64_t MAX_M = (int64_t)1 << 18;
+constexpr int64_t SKINNY_MAX_M_BF16 = 64;
+constexpr int TARGET_CUS = 256;   // MI355X compute units: split-K planning target
+constexpr size_t WS_ALIGN = 256;
+
+size_t align_up(size_t v) { return (v + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_sizes(int64_t M, int64_t d, int64_t dff, int dtype)
+{
+    if (dtype != SWIGLU_F32 && dtype != SWIGLU_BF16)
+        return SWIGLU_ERR_UNSUPPORTED;
+    if (M < 0 || d <= 0 || dff <= 0)
+        return SWIGLU_ERR_INVALID_ARG;
+    const int ve = vec_elems(dtype);
+    if (d % ve != 0 || dff % ve != 0 || d > MAX_DIM || dff > MAX_DIM || M > MAX_M)
+        return SWIGLU_ERR_UNSUPPORTED;
+    return SWIGLU_OK;
+}
+
+int check_path(int path)
+{
+    return (path == SWIGLU_PATH_AUTO || path == SWIGLU_PATH_SKINNY || path == SWIGLU_PATH_WIDE)
+               ? SWIGLU_OK
+               : SWIGLU_ERR_UNSUPPORTED;
+}
+
+// One product of the path, before a workspace is attached.
+GemmArgs up_args(int64_t M, int64_t d, int64_t dff, int dt, bool padded_out)
+{
+    GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.geom = gateup_geom(d, dff, dt);
+    g.lda = d;
+    g.M = M;
+    g.epi = EPI_SWIGLU;
+    g.dt = dt;
+    g.ldo = padded_out ? g.geom.padded_cols() : dff;
+    g.ncols_out = g.ldo;
+    return g;
+}
+
+GemmArgs down_args(int64_t M, int64_t d, int64_t dff, int dt)
+{
+    GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.geom = down_geom(d, dff, dt);
+    g.lda = gateup_geom(d, dff, dt).padded_cols();
+    g.M = M;
+    g.epi = EPI_PLAIN;
+    g.dt = dt;
+    g.ldo = d;
+    g.ncols_out = d;
+    return g;
+}
+
+// Resolves the path of one product: SKINNY or WIDE, or an error.
+int resolve_path(const GemmArgs& g, int path)
+{
+    if (path == SWIGLU_PATH_WIDE)
+        return wide_supported(g) ? SWIGLU_PATH_WIDE : SWIGLU_ERR_UNSUPPORTED;
+    if (path == SWIGLU_PATH_SKINNY)
+        return SWIGLU_PATH_SKINNY;
+    if (g.dt == DT_BF16 && g.M > SKINNY_MAX_M_BF16 && wide_supported(g))
+        return SWIGLU_PATH_WIDE;
+    return SWIGLU_PATH_SKINNY;
+}
+
+size_t partial_bytes(const GemmArgs& g, int path)
+{
+    if (path != SWIGLU_PATH_SKINNY)
+        return 0;
+    return skinny_partial_bytes(g, plan_skinny(g, TARGET_CUS));
+}
+
+size_t h_bytes(int64_t M, int64_t d, int64_t dff, int dt)
+{
+    return align_up((size_t)M * (size_t)gateup_geom(d, dff, dt).padded_cols() * elem_bytes(dt));
+}
+
+// Workspace need, or a negative status.
+int64_t workspace_need(int64_t M, int64_t d, int64_t dff, int dt, int with_down, int path)
+{
+    if (!with_down) {
+        GemmArgs u = up_args(M, d, dff, dt, false);
+        int pu = resolve_path(u, path);
+        if (pu < 0)
+            return pu;
+        return (int64_t)align_up(partial_bytes(u, pu));
+    }
+    GemmArgs u = up_args(M, d, dff, dt, true);
+    GemmArgs dn = down_args(M, d, dff, dt);
+    int pu = resolve_path(u, path), pd = resolve_path(dn, path);
+    if (pu < 0)
+        return pu;
+    if (pd < 0)
+        return pd;
+    size_t pa = partial_bytes(u, pu), pb = partial_bytes(dn, pd);
+    return (int64_t)(h_bytes(M, d, dff, dt) + align_up(pa > pb ? pa : pb));
+}
+
+int run(const GemmArgs& g, int path, void* partial, hipStream_t s)
+{
+    hipError_t e;
+    if (path == SWIGLU_PATH_WIDE)
+        e = launch_wide(g, s);
+    else
+        e = launch_skinny(g, plan_skinny(g, TARGET_CUS), (float*)partial, s);
+    return e == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_HIP;
+}
+
+int do_up(const void* x, const void* wp, void* out, int64_t M, int64_t d, int64_t dff, int dtype,
+          void* ws, size_t ws_bytes, hipStream_t s, int path)
+{
+    int rc = check_sizes(M, d, dff, dtype);
+    if (rc == SWIGLU_OK)
+        rc = check_path(path);
+    if (rc != SWIGLU_OK || M == 0)
+        return rc;
+    if (!x || !wp || !out)
+        return SWIGLU_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(wp) || !aligned16(out) || (ws && !aligned16(ws)))
+        return SWIGLU_ERR_MISALIGNED;
+    GemmArgs g = up_args(M, d, dff, dtype, false);
+    int p = resolve_path(g, path);
+    if (p < 0)
+        return p;
+    int64_t need = workspace_need(M, d, dff, dtype, 0, path);
+    if (need < 0)
+        return (int)need;
+    if ((size_t)need > ws_bytes || (need > 0 && !ws))
+        return SWIGLU_ERR_WORKSPACE;
+    g.a = x;
+    g.w = wp;
+    g.out = out;
+    return run(g, p, ws, s);
+}
+
+int do_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, int64_t d,
+           int64_t dff, int dtype, void* ws, size_t ws_bytes, hipStream_t s, int path)
+{
+    int rc = check_sizes(M, d, dff, dtype);
+    if (rc == SWIGLU_OK)
+        rc = check_path(path);
+    if (rc != SWIGLU_OK || M == 0)
+        return rc;
+    if (!x || !wp || !wdp || !y || !ws)
+        return SWIGLU_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(wp) || !aligned16(wdp) || !aligned16(y) || !aligned16(ws))
+        return SWIGLU_ERR_MISALIGNED;
+    GemmArgs u = up_args(M, d, dff, dtype, true);
+    GemmArgs dn = down_args(M, d, dff, dtype);
+    int pu = resolve_path(u, path), pd = resolve_path(dn, path);
+    if (pu < 0)
+        return pu;
+    if (pd < 0)
+        return pd;
+    int64_t need = workspace_need(M, d, dff, dtype, 1, path);
+    if (need < 0)
+        return (int)need;
+    if ((size_t)need > ws_bytes)
+        return SWIGLU_ERR_WORKSPACE;
+    uint8_t* h = (uint8_t*)ws;
+    uint8_t* partial = h + h_bytes(M, d, dff, dtype);
+    u.a = x;
+    u.w = wp;
+    u.out = h;
+    rc = run(u, pu, partial, s);
+    if (rc != SWIGLU_OK)
+        return rc;
+    dn.a = h;
+    dn.w = wdp;
+    dn.out = y;
+    return run(dn, pd, partial, s);
+}
+
+int do_pack(const void* src0, const void* src1, void* dst, const PackGeom& g, int plain,
+            hipStream_t s)
+{
+    hipError_t e = launch_pack(src0, src1, dst, g, plain, s);
+    return e == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace swg
+
+using namespace swg;
+
+extern "C" {
+
+const char* swiglu_status_string(int status)
+{
+    switch (status) {
+    case SWIGLU_OK: return "ok";
+    case SWIGLU_ERR_INVALID_ARG: return "invalid argument";
+    case SWIGLU_ERR_UNSUPPORTED: return "unsupported dtype, shape or path";
+    case SWIGLU_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case SWIGLU_ERR_WORKSPACE: return "workspace too small";
+    case SWIGLU_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int swiglu_version(void) { return 1; }
+
+size_t swiglu_packed_bytes(int64_t d, int64_t dff, int dtype)
+{
+    if (check_sizes(0, d, dff, dtype) != SWIGLU_OK)
+        return 0;
+    return (size_t)gateup_geom(d, dff, dtype).bytes();
+}
+
+size_t swiglu_down_packed_bytes(int64_t d, int64_t dff, int dtype)
+{
+    if (check_sizes(0, d, dff, dtype) != SWIGLU_OK)
+        return 0;
+    return (size_t)down_geom(d, dff, dtype).bytes();
+}
+
+size_t swiglu_workspace_bytes_ex(int64_t M, int64_t d, int64_t dff, int dtype, int with_down,
+                                 int path)
+{
+    if (check_sizes(M, d, dff, dtype) != SWIGLU_OK || check_path(path) != SWIGLU_OK || M == 0)
+        return 0;
+    int64_t need = workspace_need(M, d, dff, dtype, with_down ? 1 : 0, path);
+    return need < 0 ? 0 : (size_t)need;
+}
+
+size_t swiglu_workspace_bytes(int64_t M, int64_t d, int64_t dff, int dtype, int with_down)
+{
+    return swiglu_workspace_bytes_ex(M, d, dff, dtype, with_down, SWIGLU_PATH_AUTO);
+}
+
+int swiglu_select_path(int64_t M, int64_t d, int64_t dff, int dtype)
+{
+    int rc = check_sizes(M, d, dff, dtype);
+    if (rc != SWIGLU_OK)
+        return rc;
+    return resolve_path(up_args(M, d, dff, dtype, false), SWIGLU_PATH_AUTO);
+}
+
+int swiglu_pack_weights(const void* Wgate, const void* Wup, void* Wpacked, int64_t d, int64_t dff,
+                        int dtype, hipStream_t stream)
+{
+    int rc = check_sizes(0, d, dff, dtype);
+    if (rc != SWIGLU_OK)
+        return rc;
+    if (!Wgate || !Wup || !Wpacked)
+        return SWIGLU_ERR_INVALID_ARG;
+    if (!aligned16(Wgate) || !aligned16(Wup) || !aligned16(Wpacked))
+        return SWIGLU_ERR_MISALIGNED;
+    return do_pack(Wgate, Wup, Wpacked, gateup_geom(d, dff, dtype), 0, stream);
+}
+
+int swiglu_pack_down(const void* Wdown, void* Wdpacked, int64_t d, int64_t dff, int dtype,
+                     hipStream_t stream)
+{
+    int rc = check_sizes(0, d, dff, dtype);
+    if (rc != SWIGLU_OK)
+        return rc;
+    if (!Wdown || !Wdpacked)
+        return SWIGLU_ERR_INVALID_ARG;
+    if (!aligned16(Wdown) || !aligned16(Wdpacked))
+        return SWIGLU_ERR_MISALIGNED;
+    return do_pack(Wdown, Wdown, Wdpacked, down_geom(d, dff, dtype), 1, stream);
+}
+
+int swiglu_up(const void* x, const void* Wpacked, void* out, int64_t M, int64_t d, int64_t dff,
+              int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return do_up(x, Wpacked, out, M, d, dff, dtype, workspace, workspace_bytes, stream,
+                 SWIGLU_PATH_AUTO);
+}
+
+int swiglu_up_ex(const void* x, const void* Wpacked, void* out, int64_t M, int64_t d, int64_t dff,
+                 int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream, int path)
+{
+    return do_up(x, Wpacked, out, M, d, dff, dtype, workspace, workspace_bytes, stream, path);
+}
+
+int mlp_forward(const void* x, const void* Wpacked, const void* Wdpacked, void* y, int64_t M,
+                int64_t d, int64_t dff, int dtype, void* workspace, size_t workspace_bytes,
+                hipStream_t stream)
+{
+    return do_mlp(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace, workspace_bytes, stream,
+                  SWIGLU_PATH_AUTO);
+}
+
+int mlp_forward_ex(const void* x, const void* Wpacked, const void* Wdpacked, void* y, int64_t M,
+                   int64_t d, int64_t dff, int dtype, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream, int path)
+{
+    return do_mlp(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace, workspace_bytes, stream,
+                  path);
+}
+
+}  // extern "C"

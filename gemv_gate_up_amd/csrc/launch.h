@@ -1,0 +1,48 @@
+// launch.h -- internal host-side launchers (C++ linkage, not exported).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "geometry.h"
+
+namespace swg {
+
+// Packing (pack.hip).  plain = 0: gate/up (src0 = Wg, src1 = Wu);
+// plain = 1: down (src0 = src1 = Wd).
+hipError_t launch_pack(const void* src0, const void* src1, void* dst, const PackGeom& g,
+                       int plain, hipStream_t s);
+
+// Work description for one product of the hot path: out = epi(A . Wpacked).
+struct GemmArgs {
+    const void* a;      // activations, M x lda row-major (x, or h in the workspace)
+    int64_t lda;        // row stride of a in elements
+    const void* w;      // packed weights
+    PackGeom geom;      // geometry of w
+    void* out;          // output, M x ldo row-major
+    int64_t ldo;        // row stride of out in elements
+    int64_t ncols_out;  // output columns to store (valid columns, or the padded width)
+    int64_t M;
+    int epi;            // EPI_SWIGLU or EPI_PLAIN
+    int dt;
+};
+
+// Split-K plan for the skinny kernels.
+struct SkinnyPlan {
+    int splits;             // K splits across workgroups (1 = epilogue in the same kernel)
+    int64_t chunks_per_split;
+    int64_t grid_pb;        // pair blocks covered by the grid
+    int row_tile;           // rows per workgroup row group (bf16: 16*MT, fp32: 8)
+    int64_t row_groups;
+};
+
+SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus);
+size_t skinny_partial_bytes(const GemmArgs& g, const SkinnyPlan& p);
+
+// Skinny path (skinny.hip): weights split over workgroups, fp32 accumulation.
+hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s);
+
+// Wide path (wide.hip): bf16 MFMA GEMM with LDS double buffering.
+hipError_t launch_wide(const GemmArgs& g, hipStream_t s);
+int wide_supported(const GemmArgs& g);
+
+}  // namespace swg

@@ -1,0 +1,409 @@
+// skinny.hip -- the few-rows (decode) path: out = epi(A . W) for M <= 64.
+//
+// Follows the split-over-the-weights idea of "Où part le temps d'un token"
+// (section "Un kernel pour les matrices étroites"): with only a few rows of
+// activations the grid is cut along the weights, which are large, not along
+// the output, which is small.  Each workgroup owns one pair block of the
+// packed weights (16 gate + 16 up columns, or 32 down columns) and a range
+// of K; its four waves take interleaved K chunks, each lane streaming
+// 16-byte nontemporal loads with several in flight.  Partial sums of the
+// waves are combined in LDS in a fixed order.  When the pair blocks alone
+// do not fill the GPU, K is also split across workgroups and a second pass
+// adds the slices in ascending order; no atomics are used, so results are
+// reproducible run to run (same section: the authors reject an atomic add
+// into the output for that reason).  silu(g) * u is applied once the full
+// K sum is known (the second pass or the LDS combine), like the bias of the
+// "Affine" operation in "Deux opérations de trop".
+//
+// bf16 weights are multiplied on v_mfma_f32_16x16x32_bf16 with the
+// activations as the 16-row A operand: at M <= 16 the matrix unit has spare
+// throughput, and above M = 4 plain fp32 FMA on the VALU would take longer
+// than streaming the weights.  fp32 weights use VALU FMA.
+#include "device_common.h"
+#include "launch.h"
+
+namespace swg {
+
+constexpr int SK_WAVES = 4;
+constexpr int SK_THREADS = SK_WAVES * 64;
+
+// ---------------------------------------------------------------- bf16 (MFMA)
+template <int MT, int U, int EPI, bool SPLIT, typename OutT>
+__global__ void __launch_bounds__(SK_THREADS)
+skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
+                   const i32x4* __restrict__ w, int64_t nkc, int64_t cps,
+                   OutT* __restrict__ out, int64_t ldo, int64_t ncols_out,
+                   float* __restrict__ partial, int64_t npc, int M)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t pb = blockIdx.x;
+    const int s = blockIdx.y;
+    const int rbase = blockIdx.z * 16 * MT;
+    const int64_t kbeg = (int64_t)s * cps;
+    const int64_t kend = kbeg + cps < nkc ? kbeg + cps : nkc;
+    const i32x4* wp = w + pb * nkc * 2 * PIECE_VECS + lane;
+
+    // A operand of lane l: row l % 16 of each 16-row tile, k-group l / 16.
+    const int arow = lane & 15;
+    const int akoff = (lane >> 4) * 8;
+
+    f32x4 accg[MT], accu[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        accg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accu[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int64_t kb = kbeg + wave; kb < kend; kb += SK_WAVES * U) {
+        i32x4 wg[U], wu[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kc = kb + SK_WAVES * u;
+            if (kc < kend) {
+                wg[u] = load_nt16(wp + (kc * 2) * PIECE_VECS);
+                wu[u] = load_nt16(wp + (kc * 2 + 1) * PIECE_VECS);
+            } else {
+                wg[u] = i32x4{0, 0, 0, 0};
+                wu[u] = i32x4{0, 0, 0, 0};
+            }
+        }
+        i32x4 xa[U][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kc = kb + SK_WAVES * u;
+            const int64_t k = kc * 32 + akoff;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = rbase + mt * 16 + arow;
+                if (kc < kend && row < M && k < kvalid)
+                    xa[u][mt] = *(const i32x4*)(a + (int64_t)row * lda + k);
+                else
+                    xa[u][mt] = i32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bf16x8 bg = __builtin_bit_cast(bf16x8, wg[u]);
+            const bf16x8 bu = __builtin_bit_cast(bf16x8, wu[u]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, xa[u][mt]);
+                accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, accg[mt], 0, 0, 0);
+                accu[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, accu[mt], 0, 0, 0);
+            }
+        }
+    }
+
+    // Combine the four waves in LDS, in wave order.  MFMA result layout:
+    // lane l holds rows 4*(l/16) + i (i = 0..3) of column l % 16.
+    __shared__ float red[SK_WAVES][MT][2][64 * 4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            red[wave][mt][0][lane * 4 + i] = accg[mt][i];
+            red[wave][mt][1][lane * 4 + i] = accu[mt][i];
+        }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int r = t >> 4, c = t & 15;
+    const int src = ((r >> 2) * 16 + c) * 4 + (r & 3);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < SK_WAVES; ++wv) {
+            g += red[wv][mt][0][src];
+            u += red[wv][mt][1][src];
+        }
+        const int row = rbase + mt * 16 + r;
+        if (row >= M)
+            continue;
+        if (SPLIT) {
+            float* pr = partial + ((int64_t)s * M + row) * npc + pb * 32;
+            pr[c] = g;
+            pr[16 + c] = u;
+        } else if (EPI == EPI_SWIGLU) {
+            const int64_t n = pb * 16 + c;
+            if (n < ncols_out)
+                store_out(out + (int64_t)row * ldo + n, silu(g) * u);
+        } else {
+            const int64_t j = pb * 32 + c;
+            if (j < ncols_out)
+                store_out(out + (int64_t)row * ldo + j, g);
+            if (j + 16 < ncols_out)
+                store_out(out + (int64_t)row * ldo + j + 16, u);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- fp32 (VALU)
+// Lane l covers column l % 16 and k-group l / 16 (4 consecutive K values)
+// of each piece; the four k-groups are added with two butterfly steps whose
+// result is the same in every lane, then the waves are added in LDS.
+template <int RT, int U, int EPI, bool SPLIT, typename OutT>
+__global__ void __launch_bounds__(SK_THREADS)
+skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
+                  const f32x4* __restrict__ w, int64_t nkc, int64_t cps,
+                  OutT* __restrict__ out, int64_t ldo, int64_t ncols_out,
+                  float* __restrict__ partial, int64_t npc, int M)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t pb = blockIdx.x;
+    const int s = blockIdx.y;
+    const int rbase = blockIdx.z * RT;
+    const int64_t kbeg = (int64_t)s * cps;
+    const int64_t kend = kbeg + cps < nkc ? kbeg + cps : nkc;
+    const f32x4* wp = w + pb * nkc * 2 * PIECE_VECS + lane;
+    const int koff = (lane >> 4) * 4;
+
+    float accg[RT], accu[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        accg[r] = 0.f;
+        accu[r] = 0.f;
+    }
+
+    for (int64_t kb = kbeg + wave; kb < kend; kb += SK_WAVES * U) {
+        f32x4 wg[U], wu[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kc = kb + SK_WAVES * u;
+            if (kc < kend) {
+                wg[u] = __builtin_nontemporal_load(wp + (kc * 2) * PIECE_VECS);
+                wu[u] = __builtin_nontemporal_load(wp + (kc * 2 + 1) * PIECE_VECS);
+            } else {
+                wg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                wu[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kc = kb + SK_WAVES * u;
+            const int64_t k = kc * 16 + koff;
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int row = rbase + r;
+                if (row < M) {   // uniform across the wave
+                    f32x4 xv = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (kc < kend && k < kvalid)
+                        xv = *(const f32x4*)(a + (int64_t)row * lda + k);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        accg[r] = __builtin_fmaf(xv[e], wg[u][e], accg[r]);
+                        accu[r] = __builtin_fmaf(xv[e], wu[u][e], accu[r]);
+                    }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        accg[r] += __shfl_xor(accg[r], 16);
+        accg[r] += __shfl_xor(accg[r], 32);
+        accu[r] += __shfl_xor(accu[r], 16);
+        accu[r] += __shfl_xor(accu[r], 32);
+    }
+    __shared__ float red[SK_WAVES][2][RT][16];
+    if (lane < 16) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            red[wave][0][r][lane] = accg[r];
+            red[wave][1][r][lane] = accu[r];
+        }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t >= RT * 16)
+        return;
+    const int r = t >> 4, c = t & 15;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < SK_WAVES; ++wv) {
+        g += red[wv][0][r][c];
+        u += red[wv][1][r][c];
+    }
+    const int row = rbase + r;
+    if (row >= M)
+        return;
+    if (SPLIT) {
+        float* pr = partial + ((int64_t)s * M + row) * npc + pb * 32;
+        pr[c] = g;
+        pr[16 + c] = u;
+    } else if (EPI == EPI_SWIGLU) {
+        const int64_t n = pb * 16 + c;
+        if (n < ncols_out)
+            store_out(out + (int64_t)row * ldo + n, silu(g) * u);
+    } else {
+        const int64_t j = pb * 32 + c;
+        if (j < ncols_out)
+            store_out(out + (int64_t)row * ldo + j, g);
+        if (j + 16 < ncols_out)
+            store_out(out + (int64_t)row * ldo + j + 16, u);
+    }
+}
+
+// ---------------------------------------------------------------- second pass
+// Adds the K slices in ascending slice order, then applies the epilogue.
+template <int EPI, typename OutT>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ partial, int S, int M, int64_t npc,
+                     OutT* __restrict__ out, int64_t ldo, int64_t ncols_out, int col_blocks)
+{
+    const int row = blockIdx.x / col_blocks;
+    const int64_t col = (int64_t)(blockIdx.x % col_blocks) * 256 + threadIdx.x;
+    if (col >= ncols_out)
+        return;
+    if (EPI == EPI_SWIGLU) {
+        const int64_t pc = (col / 16) * 32 + (col % 16);
+        float g = 0.f, u = 0.f;
+        for (int s = 0; s < S; ++s) {
+            const float* pr = partial + ((int64_t)s * M + row) * npc + pc;
+            g += pr[0];
+            u += pr[16];
+        }
+        store_out(out + (int64_t)row * ldo + col, silu(g) * u);
+    } else {
+        float v = 0.f;
+        for (int s = 0; s < S; ++s)
+            v += partial[((int64_t)s * M + row) * npc + col];
+        store_out(out + (int64_t)row * ldo + col, v);
+    }
+}
+
+// ---------------------------------------------------------------- planning
+static int bf16_row_tiles(int64_t M) {
+    int64_t mt = ceil_div(M, 16);
+    return (int)(mt > 4 ? 4 : (mt < 1 ? 1 : mt));
+}
+
+static int f32_row_tile(int64_t M) {
+    return M >= 8 ? 8 : (M > 2 ? 4 : (M == 2 ? 2 : 1));
+}
+
+SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
+{
+    SkinnyPlan p;
+    p.grid_pb = ceil_div(g.ncols_out, g.geom.cols_per_pb);
+    p.row_tile = g.dt == DT_BF16 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M);
+    p.row_groups = ceil_div(g.M, p.row_tile);
+    const int64_t base = p.grid_pb * p.row_groups;
+    const int64_t target = 2 * (int64_t)num_cus;
+    const int64_t min_chunks = 8;
+    int64_t S = 1;
+    while (base * S < target && g.geom.nkc / (2 * S) >= min_chunks && S < 64)
+        S *= 2;
+    p.chunks_per_split = ceil_div(g.geom.nkc, S);
+    p.splits = (int)ceil_div(g.geom.nkc, p.chunks_per_split);
+    return p;
+}
+
+size_t skinny_partial_bytes(const GemmArgs& g, const SkinnyPlan& p)
+{
+    if (p.splits <= 1)
+        return 0;
+    return (size_t)p.splits * (size_t)g.M * (size_t)(g.geom.npb * 32) * sizeof(float);
+}
+
+template <int MT, int U, int EPI, bool SPLIT, typename OutT>
+static void go_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    dim3 grid((unsigned)p.grid_pb, (unsigned)p.splits, (unsigned)p.row_groups);
+    skinny_bf16_kernel<MT, U, EPI, SPLIT, OutT><<<grid, dim3(SK_THREADS), 0, s>>>(
+        (const uint16_t*)g.a, g.lda, g.geom.K, (const i32x4*)g.w, g.geom.nkc, p.chunks_per_split,
+        (OutT*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M);
+}
+
+template <int MT, int U, int EPI>
+static void pick_split_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    if (p.splits > 1)
+        go_bf16<MT, U, EPI, true, uint16_t>(g, p, partial, s);
+    else
+        go_bf16<MT, U, EPI, false, uint16_t>(g, p, partial, s);
+}
+
+template <int EPI>
+static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    switch (p.row_tile / 16) {
+    case 1: pick_split_bf16<1, 8, EPI>(g, p, partial, s); break;
+    case 2: pick_split_bf16<2, 8, EPI>(g, p, partial, s); break;
+    case 3: pick_split_bf16<3, 4, EPI>(g, p, partial, s); break;
+    default: pick_split_bf16<4, 4, EPI>(g, p, partial, s); break;
+    }
+}
+
+template <int RT, int U, int EPI, bool SPLIT>
+static void go_f32(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    dim3 grid((unsigned)p.grid_pb, (unsigned)p.splits, (unsigned)p.row_groups);
+    skinny_f32_kernel<RT, U, EPI, SPLIT, float><<<grid, dim3(SK_THREADS), 0, s>>>(
+        (const float*)g.a, g.lda, g.geom.K, (const f32x4*)g.w, g.geom.nkc, p.chunks_per_split,
+        (float*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M);
+}
+
+template <int RT, int EPI>
+static void pick_split_f32(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    if (p.splits > 1)
+        go_f32<RT, 8, EPI, true>(g, p, partial, s);
+    else
+        go_f32<RT, 8, EPI, false>(g, p, partial, s);
+}
+
+template <int EPI>
+static void pick_rt_f32(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    switch (p.row_tile) {
+    case 1: pick_split_f32<1, EPI>(g, p, partial, s); break;
+    case 2: pick_split_f32<2, EPI>(g, p, partial, s); break;
+    case 4: pick_split_f32<4, EPI>(g, p, partial, s); break;
+    default: pick_split_f32<8, EPI>(g, p, partial, s); break;
+    }
+}
+
+template <int EPI, typename OutT>
+static void go_reduce(const GemmArgs& g, const SkinnyPlan& p, const float* partial, hipStream_t s)
+{
+    const int col_blocks = (int)ceil_div(g.ncols_out, 256);
+    splitk_reduce_kernel<EPI, OutT><<<dim3((unsigned)(col_blocks * g.M)), dim3(256), 0, s>>>(
+        partial, p.splits, (int)g.M, g.geom.npb * 32, (OutT*)g.out, g.ldo, g.ncols_out,
+        col_blocks);
+}
+
+hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    if (g.dt == DT_BF16) {
+        if (g.epi == EPI_SWIGLU)
+            pick_mt_bf16<EPI_SWIGLU>(g, p, partial, s);
+        else
+            pick_mt_bf16<EPI_PLAIN>(g, p, partial, s);
+    } else {
+        if (g.epi == EPI_SWIGLU)
+            pick_rt_f32<EPI_SWIGLU>(g, p, partial, s);
+        else
+            pick_rt_f32<EPI_PLAIN>(g, p, partial, s);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits <= 1)
+        return e;
+    if (g.dt == DT_BF16) {
+        if (g.epi == EPI_SWIGLU)
+            go_reduce<EPI_SWIGLU, uint16_t>(g, p, partial, s);
+        else
+            go_reduce<EPI_PLAIN, uint16_t>(g, p, partial, s);
+    } else {
+        if (g.epi == EPI_SWIGLU)
+            go_reduce<EPI_SWIGLU, float>(g, p, partial, s);
+        else
+            go_reduce<EPI_PLAIN, float>(g, p, partial, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace swg

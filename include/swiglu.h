@@ -1,0 +1,154 @@
+/*
+ * swiglu.h -- C ABI of the MI355X (gfx950) fused SwiGLU MLP library.
+ *
+ * Operation (problem statement of "Tile-Level Activation Overlap for
+ * Efficient LLM Inference"; MLP block of "Anatomie d'un transformeur sur
+ * GPU", §1.1 skeleton and §1.2 projection table):
+ *
+ *     out = silu(x . Wgate) (.) (x . Wup),     silu(z) = z * sigmoid(z)
+ *     y   = out . Wdown                         (mlp_forward only)
+ *
+ * with x: M x d, Wgate and Wup: d x dff, Wdown: dff x d, out: M x dff,
+ * y: M x d.  All matrices are row-major and dense.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named x, w*, out, y and workspace are DEVICE pointers on the
+ *     current HIP device; the caller allocates and owns them.  The library
+ *     keeps no pointer after a call returns and holds no mutable global
+ *     state, so calls are thread-safe.
+ *   - dtype is SWIGLU_BF16 (bf16 storage, fp32 accumulation, bf16 output)
+ *     or SWIGLU_F32 (fp32 storage and arithmetic).  x, the weights and the
+ *     output share one dtype.
+ *   - Calls only enqueue kernels on `stream`: no allocation, no copy, no
+ *     synchronisation (the decode-path conventions of "Où part le temps d'un
+ *     token": fixed buffers, no per-call allocation, no host waits).  A
+ *     return of SWIGLU_OK means the arguments were valid and the launches
+ *     were accepted; faults during execution surface at the caller's next
+ *     synchronisation.
+ *   - Results are deterministic: the same inputs, shapes and device give
+ *     bitwise identical outputs on every call (no atomics in any sum).
+ *   - Errors are returned as negative status codes; nothing throws.  When
+ *     M == 0 every call is a no-op returning SWIGLU_OK, and pointers may be
+ *     NULL.
+ *   - Requirements: d and dff multiples of 8 (bf16) or 4 (fp32); device
+ *     pointers 16-byte aligned; 1 <= d, dff <= 2^20; 0 <= M <= 2^18.
+ *     Otherwise SWIGLU_ERR_UNSUPPORTED / SWIGLU_ERR_MISALIGNED.
+ *   - out, y and the workspace must not overlap any input.
+ */
+#ifndef SWIGLU_H
+#define SWIGLU_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum swiglu_dtype {
+    SWIGLU_F32 = 0,
+    SWIGLU_BF16 = 1
+} swiglu_dtype_t;
+
+typedef enum swiglu_status {
+    SWIGLU_OK = 0,
+    SWIGLU_ERR_INVALID_ARG = -1,   /* NULL pointer, negative M, d or dff <= 0 */
+    SWIGLU_ERR_UNSUPPORTED = -2,   /* unknown dtype, unsupported shape or path */
+    SWIGLU_ERR_MISALIGNED = -3,    /* a device pointer is not 16-byte aligned */
+    SWIGLU_ERR_WORKSPACE = -4,     /* workspace smaller than required */
+    SWIGLU_ERR_HIP = -5            /* a HIP launch or attribute call failed */
+} swiglu_status_t;
+
+/* Path selection for the *_ex entry points. */
+typedef enum swiglu_path {
+    SWIGLU_PATH_AUTO = 0,      /* dispatcher: few rows -> skinny, many rows -> wide */
+    SWIGLU_PATH_SKINNY = 1,    /* split-over-weights kernels (any M, any dtype) */
+    SWIGLU_PATH_WIDE = 2       /* bf16 MFMA GEMM with LDS double buffering */
+} swiglu_path_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *swiglu_status_string(int status);
+
+/* Library ABI version (incremented on any incompatible change). */
+int swiglu_version(void);
+
+/*
+ * Size in bytes of the fused gate/up buffer written by swiglu_pack_weights,
+ * or 0 for invalid arguments.  The buffer is opaque: gate and up column
+ * blocks interleaved (the fused K x 2N weight of Kernel-2 in "Tile-Level
+ * Activation Overlap for Efficient LLM Inference"), padded with zeros.
+ */
+size_t swiglu_packed_bytes(int64_t d, int64_t dff, int dtype);
+
+/* Size in bytes of the packed down weight written by swiglu_pack_down. */
+size_t swiglu_down_packed_bytes(int64_t d, int64_t dff, int dtype);
+
+/*
+ * Workspace bytes a call with these sizes needs (0 if none), for
+ * swiglu_up (with_down = 0) or mlp_forward (with_down = 1) on the automatic
+ * path; the _ex variant gives the size for a forced path.  Returns 0 for
+ * invalid arguments as well, which the calls then reject.
+ */
+size_t swiglu_workspace_bytes(int64_t M, int64_t d, int64_t dff, int dtype, int with_down);
+size_t swiglu_workspace_bytes_ex(int64_t M, int64_t d, int64_t dff, int dtype, int with_down,
+                                 int path);
+
+/* The path SWIGLU_PATH_AUTO takes for these sizes (SKINNY or WIDE), or a
+ * negative status for invalid arguments. */
+int swiglu_select_path(int64_t M, int64_t d, int64_t dff, int dtype);
+
+/*
+ * Packs Wgate and Wup (each d x dff, row-major, device) into Wpacked (device,
+ * swiglu_packed_bytes(d, dff, dtype) bytes).  Done once per weight set; the
+ * packed buffer then serves every M and both paths.  Pure permutation with
+ * zero padding: no rounding.  Wpacked must not overlap Wgate or Wup.
+ */
+int swiglu_pack_weights(const void *Wgate, const void *Wup, void *Wpacked,
+                        int64_t d, int64_t dff, int dtype, hipStream_t stream);
+
+/*
+ * Packs Wdown (dff x d, row-major, device) into Wdpacked (device,
+ * swiglu_down_packed_bytes(d, dff, dtype) bytes) for mlp_forward.
+ */
+int swiglu_pack_down(const void *Wdown, void *Wdpacked, int64_t d, int64_t dff, int dtype,
+                     hipStream_t stream);
+
+/*
+ * out (M x dff) = silu(x . Wgate) (.) (x . Wup), with x M x d and Wpacked
+ * from swiglu_pack_weights.  Accumulation in fp32; silu and the product in
+ * fp32; one rounding to the output dtype at the store.  workspace (device,
+ * may be NULL when swiglu_workspace_bytes returns 0) holds split-K partial
+ * sums on the skinny path.
+ */
+int swiglu_up(const void *x, const void *Wpacked, void *out,
+              int64_t M, int64_t d, int64_t dff, int dtype,
+              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* swiglu_up with a forced path (swiglu_path_t); WIDE with fp32 returns
+ * SWIGLU_ERR_UNSUPPORTED. */
+int swiglu_up_ex(const void *x, const void *Wpacked, void *out,
+                 int64_t M, int64_t d, int64_t dff, int dtype,
+                 void *workspace, size_t workspace_bytes, hipStream_t stream, int path);
+
+/*
+ * y (M x d) = (silu(x . Wgate) (.) (x . Wup)) . Wdown: the MLP of the layer
+ * skeleton, with Wpacked from swiglu_pack_weights and Wdpacked from
+ * swiglu_pack_down.  The intermediate h (M x dff) is kept in the workspace
+ * in the storage dtype (bf16 or fp32), then multiplied by Wdown with fp32
+ * accumulation.
+ */
+int mlp_forward(const void *x, const void *Wpacked, const void *Wdpacked, void *y,
+                int64_t M, int64_t d, int64_t dff, int dtype,
+                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* mlp_forward with a forced path for both products. */
+int mlp_forward_ex(const void *x, const void *Wpacked, const void *Wdpacked, void *y,
+                   int64_t M, int64_t d, int64_t dff, int dtype,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream, int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_H */

@@ -1,0 +1,110 @@
+"""Host-only checks of the C-ABI library: it loads without a GPU, exports
+every function include/swiglu.h declares, and rejects bad arguments before
+any HIP call (so these run on a CPU-only machine)."""
+import subprocess
+
+import pytest
+
+import gemv_gate_up_amd as sw
+import workloads as wl
+
+BF16, F32 = sw.SWIGLU_BF16, sw.SWIGLU_F32
+FAKE = 0x10000000    # 16-byte aligned address that is never dereferenced here
+
+
+def test_header_symbols_are_exported():
+    names = sw.header_functions()
+    assert {"swiglu_pack_weights", "swiglu_up", "mlp_forward", "swiglu_pack_down"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", sw.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+
+
+def test_status_strings_and_version():
+    assert sw.swiglu_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert sw.swiglu_status_string(code) != "unknown status"
+    assert sw.swiglu_status_string(17) == "unknown status"
+
+
+def test_packed_sizes():
+    # 8B-class: two 4096 x 14336 bf16 matrices, no padding needed
+    assert sw.swiglu_packed_bytes(4096, 14336, BF16) == 2 * 4096 * 14336 * 2
+    # 72B-class: dff = 29568 = 231 * 128 fits whole 256-column tiles
+    assert sw.swiglu_packed_bytes(8192, 29568, BF16) == 968884224
+    assert sw.swiglu_down_packed_bytes(8192, 29568, BF16) == 484442112
+    # fp32 tiny decode
+    assert sw.swiglu_packed_bytes(512, 2048, F32) == 2 * 512 * 2048 * 4
+    # ragged shapes pad K to 64 (bf16) and columns to 128
+    assert sw.swiglu_packed_bytes(1000, 1400, BF16) == 1024 * 1408 * 2 * 2
+    assert sw.swiglu_packed_bytes(0, 16, BF16) == 0
+    assert sw.swiglu_packed_bytes(16, 16, 7) == 0
+
+
+def test_dispatcher():
+    for M in (1, 4, 8, 16, 17, 32, 64):
+        assert sw.swiglu_select_path(M, 4096, 14336, BF16) == sw.SWIGLU_PATH_SKINNY
+    for M in (65, 128, 2048, 4096):
+        assert sw.swiglu_select_path(M, 4096, 14336, BF16) == sw.SWIGLU_PATH_WIDE
+    for M in (1, 64, 4096):
+        assert sw.swiglu_select_path(M, 512, 2048, F32) == sw.SWIGLU_PATH_SKINNY
+    assert sw.swiglu_select_path(1, 4096, 14336, 9) == sw.SWIGLU_ERR_UNSUPPORTED
+    assert sw.swiglu_select_path(-1, 4096, 14336, BF16) == sw.SWIGLU_ERR_INVALID_ARG
+
+
+def test_workspace_sizes():
+    # decode: the pair blocks fill the GPU, no split-K partials needed
+    assert sw.swiglu_workspace_bytes(1, 4096, 14336, BF16, 0) == 0
+    # tiny fp32 decode splits K four ways: 4 x 1 x 4096 fused columns x 4 B
+    assert sw.swiglu_workspace_bytes(1, 512, 2048, F32, 0) == 4 * 4096 * 4
+    # full MLP keeps h (M x padded dff) in the workspace
+    assert sw.swiglu_workspace_bytes(2048, 8192, 29568, BF16, 1) >= 2048 * 29568 * 2
+    assert sw.swiglu_workspace_bytes_ex(4096, 512, 2048, F32, 0, sw.SWIGLU_PATH_WIDE) == 0
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_argument_errors_return_before_any_launch(dtype):
+    M, d, dff = 4, 64, 64
+    up = lambda *a, **k: sw.swiglu_up(*a, stream=0, **k)
+    assert up(FAKE, FAKE, FAKE, -1, d, dff, dtype) == sw.SWIGLU_ERR_INVALID_ARG
+    assert up(FAKE, FAKE, FAKE, M, 0, dff, dtype) == sw.SWIGLU_ERR_INVALID_ARG
+    assert up(FAKE, FAKE, FAKE, M, d, -8, dtype) == sw.SWIGLU_ERR_INVALID_ARG
+    assert up(FAKE, FAKE, FAKE, M, d, dff, 5) == sw.SWIGLU_ERR_UNSUPPORTED
+    assert up(FAKE, FAKE, FAKE, M, 6, dff, dtype) == sw.SWIGLU_ERR_UNSUPPORTED
+    assert up(FAKE, FAKE, FAKE, M, d, (1 << 20) + 8, dtype) == sw.SWIGLU_ERR_UNSUPPORTED
+    assert up(None, FAKE, FAKE, M, d, dff, dtype) == sw.SWIGLU_ERR_INVALID_ARG
+    assert up(FAKE, None, FAKE, M, d, dff, dtype) == sw.SWIGLU_ERR_INVALID_ARG
+    assert up(FAKE + 4, FAKE, FAKE, M, d, dff, dtype) == sw.SWIGLU_ERR_MISALIGNED
+    assert up(FAKE, FAKE, FAKE + 8, M, d, dff, dtype) == sw.SWIGLU_ERR_MISALIGNED
+    # M == 0 is a no-op, whatever the pointers
+    assert up(None, None, None, 0, d, dff, dtype) == sw.SWIGLU_OK
+    assert sw.mlp_forward(None, None, None, None, 0, d, dff, dtype, stream=0) == sw.SWIGLU_OK
+    assert sw.mlp_forward(FAKE, FAKE, FAKE, FAKE, M, d, dff, dtype, None, 0,
+                          stream=0) == sw.SWIGLU_ERR_INVALID_ARG
+    assert sw.swiglu_pack_weights(FAKE, None, FAKE, d, dff, dtype, 0) == sw.SWIGLU_ERR_INVALID_ARG
+    assert sw.swiglu_pack_weights(FAKE, FAKE + 2, FAKE, d, dff, dtype, 0) == sw.SWIGLU_ERR_MISALIGNED
+    assert sw.swiglu_pack_down(FAKE, FAKE, d, 0, dtype, 0) == sw.SWIGLU_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_is_rejected():
+    # tiny fp32 decode needs split-K partials; none are given
+    rc = sw.swiglu_up(FAKE, FAKE, FAKE, 1, 512, 2048, F32, None, 0, stream=0)
+    assert rc == sw.SWIGLU_ERR_WORKSPACE
+    need = sw.swiglu_workspace_bytes(64, 896, 4864, BF16, 1)
+    rc = sw.mlp_forward(FAKE, FAKE, FAKE, FAKE, 64, 896, 4864, BF16, FAKE, need - 256, stream=0)
+    assert rc == sw.SWIGLU_ERR_WORKSPACE
+
+
+def test_forced_paths():
+    rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, F32, None, 0, 0, sw.SWIGLU_PATH_WIDE)
+    assert rc == sw.SWIGLU_ERR_UNSUPPORTED
+    rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, BF16, None, 0, 0, 3)
+    assert rc == sw.SWIGLU_ERR_UNSUPPORTED
+
+
+def test_workloads_shapes_are_supported():
+    for w in wl.WORKLOADS.values():
+        assert sw.swiglu_packed_bytes(w.d, w.dff, w.dtype) > 0
+        assert sw.swiglu_select_path(w.M, w.d, w.dff, w.dtype) in (1, 2)

@@ -1,0 +1,77 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+bench times (automatic path), against the oracle: every output where the
+oracle finishes in seconds, else whole sampled rows spread over tiles and
+the ragged last tile."""
+import numpy as np
+import torch  # noqa: F401  (first import on a fresh box is slow; keep it out of test timeouts)
+import pytest
+
+import oracle
+import workloads as wl
+from swiglu_testlib import assert_close, dev, host, pack, run_mlp, run_up, say
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _inputs(name):
+    w = wl.WORKLOADS[name]
+    key = (w.cfg, w.with_down)
+    if key not in _cache:
+        _cache.clear()
+        full = wl.WORKLOADS[name]
+        inp = wl.make_inputs(full, M=full.m_max)
+        wp, wdp = pack(inp, w.d, w.dff, w.dtype)
+        _cache[key] = (inp, wp, wdp)
+    return _cache[key]
+
+
+def _rows(M):
+    if M <= 64:
+        return None                    # all rows
+    cand = [0, 1, 127, 128, 255, 256, M // 2 + 3, M - 257, M - 2, M - 1]
+    return sorted({r for r in cand if 0 <= r < M})
+
+
+@pytest.mark.parametrize("name", ["tiny_decode_f32", "decode8b_m1", "decode8b_m4", "decode8b_m8",
+                                  "decode8b_m16", "prefill8b_m4096"])
+def test_up_workload(name):
+    w = wl.WORKLOADS[name]
+    say("workload", name, w)
+    inp, wp, _ = _inputs(name)
+    x = inp["x"][:w.M]
+    out = run_up(dev(x), wp, w.M, w.d, w.dff, w.dtype)
+    rows = _rows(w.M)
+    got = host(out if rows is None else out[rows], w.dtype)
+    ref = oracle.swiglu(x, inp["wg"], inp["wu"], rows=rows)
+    st = assert_close(got, ref, w.dtype, name)
+    say(name, st)
+
+
+@pytest.mark.parametrize("name", ["mlp05b_m64", "mlp72b_m16", "mlp72b_m2048"])
+def test_mlp_workload(name):
+    w = wl.WORKLOADS[name]
+    say("workload", name, w)
+    inp, wp, wdp = _inputs(name)
+    x = inp["x"][:w.M]
+    y = run_mlp(dev(x), wp, wdp, w.M, w.d, w.dff, w.dtype)
+    rows = _rows(w.M)
+    got = host(y if rows is None else y[rows], w.dtype)
+    ref = oracle.mlp(x, inp["wg"], inp["wu"], inp["wd"], rows=rows)
+    st = assert_close(got, ref, w.dtype, name)
+    say(name, st)
+
+
+def test_mlp72b_tensor_parallel_shard():
+    # One GPU's share of the 72B-class MLP split eight ways over d_ff
+    # (29568 / 8 = 3696 columns, not a multiple of the 128-column tile).
+    d, dff = 8192, 3696
+    for M in (16, 300):
+        say("tp shard", M, d, dff)
+        inp = wl.random_inputs(5000 + M, M, d, dff, wl.BF16, with_down=True)
+        wp, wdp = pack(inp, d, dff, wl.BF16)
+        y = host(run_mlp(dev(inp["x"]), wp, wdp, M, d, dff, wl.BF16), wl.BF16)
+        rows = _rows(M)
+        ref = oracle.mlp(inp["x"], inp["wg"], inp["wu"], inp["wd"], rows=rows)
+        assert_close(y if rows is None else y[rows], ref, wl.BF16, "tp shard M=%d" % M)

@@ -80,9 +80,10 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (round to nearest, ties to even); returns
     the raw 16-bit patterns as uint16.  NaN inputs are not expected."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    u = a.view(np.uint32)
+    # finite inputs: u + 0x8000 stays below 2**32 (largest is 0xFF7FFFFF)
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
