@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused SwiGLU MLP hot path on one MI355X.
+
+One step = one call of the hot path (swiglu_up / mlp_forward through the C
+ABI) on resident inputs.  The headline line is the 8B-class decode step
+(M = 1, d = 4096, d_ff = 14336, bf16) in HBM GB/s of algorithmic traffic
+(both weight matrices once, x once, the output once); the same JSON line also
+carries the 8B-class prefill step (M = 4096) in bf16 TFLOP/s.
+
+Weights are rotated through a ring of copies (>= 1 GB in total) so that the
+256 MB Infinity Cache cannot serve a repeated call: every timed call streams
+its weights from HBM.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+F32_VALU_PEAK_TFLOPS = 157.3
+METRIC = "fused SwiGLU MLP: HBM GB/s at M=1 decode; bf16 TFLOP/s at M=4096 prefill"
+KERNEL_SOURCES = ["geometry.h", "device_common.h", "launch.h", "api.hip", "pack.hip",
+                  "skinny.hip", "wide.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gemv_gate_up_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("src_sha") != kernel_source_hash() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Runner:
+    """Device buffers and the C-ABI call for one workload."""
+
+    def __init__(self, w: wl.Workload, copies: int):
+        import torch
+        import gemv_gate_up_amd as sw
+        self.torch, self.sw, self.w = torch, sw, w
+        t0 = time.time()
+        self.inp = wl.make_inputs(w, M=w.M)
+        log("inputs for %s generated in %.1fs" % (w.name, time.time() - t0))
+        tdt = torch.int16 if w.dtype == wl.BF16 else torch.float32
+
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to("cuda")
+
+        self.x = dev(self.inp["x"])
+        wp = torch.empty(sw.swiglu_packed_bytes(w.d, w.dff, w.dtype), dtype=torch.uint8,
+                         device="cuda")
+        sw.check(sw.swiglu_pack_weights(dev(self.inp["wg"]), dev(self.inp["wu"]), wp, w.d, w.dff,
+                                        w.dtype), "pack")
+        self.wps = [wp] + [wp.clone() for _ in range(copies - 1)]
+        self.wdps = [None] * copies
+        if w.with_down:
+            wdp = torch.empty(sw.swiglu_down_packed_bytes(w.d, w.dff, w.dtype), dtype=torch.uint8,
+                              device="cuda")
+            sw.check(sw.swiglu_pack_down(dev(self.inp["wd"]), wdp, w.d, w.dff, w.dtype), "pack")
+            self.wdps = [wdp] + [wdp.clone() for _ in range(copies - 1)]
+        ncols = w.d if w.with_down else w.dff
+        self.out = torch.empty((w.M, ncols), dtype=tdt, device="cuda")
+        self.ws_bytes = sw.swiglu_workspace_bytes(w.M, w.d, w.dff, w.dtype, int(w.with_down))
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream()
+        self.sh = self.stream.cuda_stream
+        self.copies = copies
+        self.path = sw.swiglu_select_path(w.M, w.d, w.dff, w.dtype)
+        # raw pointers once, so a step is a single foreign call
+        self.args = [(self.x.data_ptr(), self.wps[i].data_ptr(),
+                      self.wdps[i].data_ptr() if self.wdps[i] is not None else None)
+                     for i in range(copies)]
+
+    def step(self, i: int) -> None:
+        w, sw = self.w, self.sw
+        xp, wpp, wdpp = self.args[i % self.copies]
+        if w.with_down:
+            rc = sw._lib.mlp_forward(xp, wpp, wdpp, self.out.data_ptr(), w.M, w.d, w.dff, w.dtype,
+                                     self.ws.data_ptr(), self.ws_bytes, self.sh)
+        else:
+            rc = sw._lib.swiglu_up(xp, wpp, self.out.data_ptr(), w.M, w.d, w.dff, w.dtype,
+                                   self.ws.data_ptr(), self.ws_bytes, self.sh)
+        if rc != 0:
+            raise RuntimeError("step failed: %s" % sw.swiglu_status_string(rc))
+
+    def time(self, steps: int, warmup: int) -> dict:
+        """Two passes over the same K steps: first back-to-back launches
+        timed by the host clock between synchronisations (the step rate),
+        then the same launches bracketed one by one with HIP events on the
+        launch stream (the kernel duration of one launch)."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record(self.stream)
+            self.step(warmup + steps + i)
+            evs[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        durs = np.array([a.elapsed_time(b) for a, b in evs])   # ms
+        return {"wall_ms_per_step": (t1 - t0) * 1e3 / steps,
+                "event_ms_mean": float(durs.mean()), "event_ms_median": float(np.median(durs)),
+                "event_ms_min": float(durs.min()), "event_ms_max": float(durs.max())}
+
+
+def dominant_kernel(w: wl.Workload, path: int) -> str:
+    if path == 2:
+        return "wide_bf16_kernel"
+    return "skinny_bf16_kernel" if w.dtype == wl.BF16 else "skinny_f32_kernel"
+
+
+def measure(w: wl.Workload, steps: int, warmup: int, copies: int) -> dict:
+    r = Runner(w, copies)
+    t = r.time(steps, warmup)
+    kern = dominant_kernel(w, r.path)
+    per_launch_ms = t["event_ms_mean"]
+    single_kernel = (not w.with_down) and (
+        r.path == 2 or r.sw.swiglu_workspace_bytes(w.M, w.d, w.dff, w.dtype, 0) == 0)
+    res = {"runner": r, "timing": t, "kernel": kern, "path": r.path,
+           "single_kernel_step": single_kernel}
+    bytes_alg = w.algorithmic_bytes()
+    flops_alg = w.algorithmic_flops()
+    hbm_bound = flops_alg / bytes_alg < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if hbm_bound:
+        achieved = bytes_alg / (per_launch_ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops_alg / (per_launch_ms * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1),
+                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    res["roofline"]["traffic"] = traffic_from_profile(w.name, kern)
+    res["roofline"]["kernel"] = kern
+    res["roofline"]["kernel_ms"] = round(per_launch_ms, 5)
+    return res
+
+
+def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float) -> dict:
+    """The oracle, as it stands, on the host cores: full workload calls
+    repeated for about budget_s seconds (at least one)."""
+    import oracle
+    threads = oracle.available_cores()
+    x = inp["x"][:w.M]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if w.with_down:
+            oracle.mlp(x, inp["wg"], inp["wu"], inp["wd"], nthreads=threads)
+        else:
+            oracle.swiglu(x, inp["wg"], inp["wu"], nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_call = el / reps
+    return {"value": round(w.algorithmic_bytes() / per_call / 1e9, 3), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "%d full %s call(s) (M=%d, d=%d, dff=%d) in %.1f s wall, fp64" % (
+                reps, w.name, w.M, w.d, w.dff, el),
+            "ms_per_call": round(per_call * 1e3, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode8b_m1", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(one GPU's share of a sharded MLP is the same kernel at a smaller d_ff).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = wl.WORKLOADS[args.workload]
+    one_copy = 2 * w.d * w.dff * w.elem_bytes
+    copies = max(1, -(-(1 << 30) // one_copy)) if one_copy < (1 << 30) else 1
+    log("workload %s: %s, %d weight copies" % (w.name, w, copies))
+    m = measure(w, args.steps, args.warmup, copies)
+    t = m["timing"]
+    value_bytes = w.algorithmic_bytes() / (t["wall_ms_per_step"] * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value_bytes, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["wall_ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights, bf16 RNE)",
+        "config": {"workload": w.name, "M": w.M, "d": w.d, "dff": w.dff,
+                   "with_down": w.with_down, "path": "skinny" if m["path"] == 1 else "wide",
+                   "weight_copies": copies, "algorithmic_bytes": w.algorithmic_bytes(),
+                   "algorithmic_flops": w.algorithmic_flops()},
+        "roofline": m["roofline"],
+        "timing_ms": {k: round(v, 5) for k, v in t.items()},
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, m["runner"].inp, args.cpu_seconds)
+    del m
+    torch.cuda.empty_cache()
+    if not args.no_prefill and w.name != "prefill8b_m4096":
+        p = wl.WORKLOADS["prefill8b_m4096"]
+        mp = measure(p, args.prefill_steps, 3, 1)
+        tp = mp["timing"]
+        rec["prefill"] = {
+            "workload": p.name, "M": p.M, "d": p.d, "dff": p.dff,
+            "value": round(p.algorithmic_flops() / (tp["wall_ms_per_step"] * 1e-3) / 1e12, 1),
+            "unit": "TFLOP/s", "ms_per_step": round(tp["wall_ms_per_step"], 4),
+            "steps": args.prefill_steps, "warmup": 3, "roofline": mp["roofline"],
+            "timing_ms": {k: round(v, 5) for k, v in tp.items()},
+        }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
