@@ -34,7 +34,7 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 F32_VALU_PEAK_TFLOPS = 157.3
 METRIC = "fused SwiGLU MLP: HBM GB/s at M=1 decode; bf16 TFLOP/s at M=4096 prefill"
 KERNEL_SOURCES = ["geometry.h", "device_common.h", "launch.h", "api.hip", "pack.hip",
-                  "skinny.hip", "wide.hip"]
+                  "skinny.hip", "wide.hip", "wide_kernel.h"]
 
 
 def log(*a):

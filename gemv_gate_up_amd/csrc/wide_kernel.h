@@ -1,0 +1,334 @@
+// wide_kernel.h -- the many-rows (prefill) MFMA GEMM, templated on its tile
+// shape and pipeline depth; wide.hip instantiates the configuration used.
+//
+// This is the interleaved single-GEMM design of "Tile-Level Activation
+// Overlap for Efficient LLM Inference" (Kernel-2): one GEMM over M x 2N x K
+// on the fused weight, whose accumulator tile holds gate and up columns side
+// by side; the epilogue stores silu(gate) * up, so the gate and up
+// intermediates never reach HBM.  Built for gfx950 as follows:
+//   * block tile BM x BN (BN counts fused columns: BN/32 pair blocks of 16
+//     gate + 16 up columns); a pipeline stage holds KCS chunks of 32 K;
+//   * both operands go global -> LDS with buffer_load ... lds (no VGPR
+//     staging) into pieces that are exactly MFMA operand fragments, so every
+//     ds_read_b128 is conflict free;
+//   * STAGES LDS buffers in a ring, up to STAGES - 1 stages in flight; one
+//     barrier per stage publishes stage t+1, whose fragments are then read
+//     into registers behind stage t's MFMAs (v_mfma_f32_16x16x32_bf16), so
+//     LDS latency hides behind matrix work;
+//   * pairing block = MFMA N fragment (16 columns): lane l holds gate and up
+//     of the same output element, so the epilogue needs no lane exchange;
+//   * tiles are remapped so each XCD (own L2) works through a compact group
+//     of tiles that share A row panels and B column panels.
+// The down projection runs through the same kernel with a plain epilogue.
+#pragma once
+#include "device_common.h"
+#include "launch.h"
+
+namespace swg {
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the release fence of __syncthreads (which would
+// wait for every outstanding load, including the stages still in flight).
+// LDS is written only by the buffer loads, whose completion each wave awaits
+// with wait_vmcnt before arriving.  lgkmcnt(0) retires this wave's LDS reads
+// before any wave may overwrite the buffer they read; it is issued through
+// the builtin so that the compiler knows those reads are complete and does
+// not wait again before MFMAs that use them.  The "memory" clobber keeps
+// the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited
+    asm volatile("s_barrier" ::: "memory");
+}
+
+constexpr uint32_t OOB_OFFSET = 0x80000000u;   // any offset >= num_records reads zero
+
+// Raw buffer descriptor (base, stride 0, num_records bytes) in four SGPRs.
+__device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t num_bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+    r.z = __builtin_amdgcn_readfirstlane((int)num_bytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane, global -> LDS at lds_base + 16 * lane, bypassing VGPRs.
+// Issued through inline asm so that the compiler does not add a blanket
+// vmcnt(0) before LDS reads; completion is awaited with wait_vmcnt.
+__device__ __forceinline__ void load_lds16(const i32x4& srd, uint32_t voffset,
+                                           uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(srd), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES>
+struct WideShape {
+    static constexpr int NW = WGM * WGN;
+    static constexpr int THREADS = NW * 64;
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int PB_TILE = BN / 32;
+    static constexpr int A_PIECES = (BM / 16) * KCS;      // [row block][chunk]
+    static constexpr int B_PIECES = PB_TILE * KCS * 2;    // [pair block][chunk][half]
+    static constexpr int PIECES = A_PIECES + B_PIECES;
+    static constexpr int PPW = PIECES / NW;               // loads per wave per stage
+    static constexpr int APW = A_PIECES / NW;
+    static constexpr int STAGE_BYTES = PIECES * PIECE_BYTES;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static_assert(PIECES % NW == 0 && A_PIECES % NW == 0, "pieces must split evenly");
+    static_assert(FN % 2 == 0, "a wave tile holds whole pair blocks");
+    static_assert(STAGES >= 3, "stage t+1 must be in flight before step t starts");
+    static_assert((STAGES - 2) * PPW < 64, "vmcnt budget");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int PPW, int MAXA>
+__device__ __forceinline__ void wait_stage(int ahead) {
+    // wait until at most `ahead` later stages of this wave remain in flight
+    if (MAXA >= 3 && ahead >= 3) { wait_vmcnt<(MAXA >= 3 ? 3 : 0) * PPW>(); return; }
+    if (MAXA >= 2 && ahead >= 2) { wait_vmcnt<(MAXA >= 2 ? 2 : 0) * PPW>(); return; }
+    if (MAXA >= 1 && ahead >= 1) { wait_vmcnt<PPW>(); return; }
+    wait_vmcnt<0>();
+}
+
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI>
+__global__ void __launch_bounds__(WGM * WGN * 64, 1)
+wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, int M,
+                 const uint16_t* __restrict__ w, int64_t nkc, int64_t npb,
+                 uint16_t* __restrict__ out, int64_t ldo, int64_t ncols_out,
+                 int tiles_m, int tiles_n, int group_m)
+{
+    using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES>;
+    constexpr int FM = S::FM, FN = S::FN, PPW = S::PPW, APW = S::APW, NW = S::NW;
+    constexpr int A_PIECES = S::A_PIECES;
+
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+
+    // ---- tile coordinates: XCD-contiguous ranges, then grouped raster
+    int pid = blockIdx.x;
+    const int G = tiles_m * tiles_n;
+    const int per_xcd = G / 8;
+    if (pid < per_xcd * 8)
+        pid = (pid % 8) * per_xcd + pid / 8;
+    const int in_group = group_m * tiles_n;
+    const int first_m = (pid / in_group) * group_m;
+    const int gsz = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    const int tm = first_m + (pid % in_group) % gsz;
+    const int tn = (pid % in_group) / gsz;
+
+    const int m0 = tm * BM;
+    const int64_t pb0 = (int64_t)tn * S::PB_TILE;
+    const int rows_here = M - m0 < BM ? M - m0 : BM;
+    const i32x4 ra = make_srd(a + (int64_t)m0 * lda, (uint32_t)((int64_t)rows_here * lda * 2));
+    // pair blocks past the packed buffer read as zero
+    const int64_t pbs_here = npb - pb0 < S::PB_TILE ? npb - pb0 : S::PB_TILE;
+    const i32x4 rw = make_srd(w + pb0 * nkc * 2 * 512,
+                              (uint32_t)(pbs_here * nkc * 2 * PIECE_BYTES));
+    const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void_t*)smem;
+
+    // ---- per-lane byte offsets of this wave's pieces in stage 0
+    uint32_t off[PPW];
+    int akk[APW > 0 ? APW : 1];
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+        const int q = wave + j * NW;
+        if (j < APW) {
+            const int rb = q / KCS, kc = q % KCS;
+            const int row = rb * 16 + (lane & 15);
+            const int kk = kc * 32 + (lane >> 4) * 8;
+            akk[j] = kk;
+            off[j] = (uint32_t)(((int64_t)row * lda + kk) * 2);
+        } else {
+            const int qb = q - A_PIECES;
+            const int pbl = qb / (KCS * 2), kc = (qb / 2) % KCS, half = qb & 1;
+            off[j] = (uint32_t)(((int64_t)(pbl * nkc + kc) * 2 + half) * PIECE_BYTES + lane * 16);
+        }
+    }
+
+    auto load_stage = [&](int64_t t) {
+        const uint32_t base = smem_base + (uint32_t)((t % STAGES) * S::STAGE_BYTES);
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {
+            const int q = wave + j * NW;
+            const uint32_t dst =
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + q * PIECE_BYTES));
+            if (j < APW) {
+                const int64_t k = t * (KCS * 32) + akk[j];
+                const uint32_t o =
+                    k < kvalid ? off[j] + (uint32_t)(t * (KCS * 64)) : OOB_OFFSET;
+                load_lds16(ra, o, dst);
+            } else {
+                load_lds16(rw, off[j] + (uint32_t)(t * (KCS * 2 * PIECE_BYTES)), dst);
+            }
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t nsteps = nkc / KCS;
+
+    // Operand fragments in registers.  A fragments are double buffered;
+    // each B fragment is refilled from the next stage as soon as the MFMAs
+    // of the current stage that use it have been issued (B outer, A inner),
+    // which keeps one B set live instead of two.
+    struct AFrags {
+        bf16x8 v[KCS][FM];
+    };
+    struct BFrags {
+        bf16x8 v[KCS][FN];
+    };
+    auto stage_ptr = [&](int64_t t) {
+        return smem + (t % STAGES) * S::STAGE_BYTES + lane * 16;
+    };
+    auto read_a = [&](int64_t t, AFrags& f) {
+        const uint8_t* base = stage_ptr(t);
+#pragma unroll
+        for (int kc = 0; kc < KCS; ++kc)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                f.v[kc][fm] = *(const bf16x8*)(base + ((wm * FM + fm) * KCS + kc) * PIECE_BYTES);
+    };
+    auto read_b = [&](const uint8_t* base, int kc, int fn) {
+        const int idx = wn * FN + fn;
+        const int piece = A_PIECES + ((idx >> 1) * KCS + kc) * 2 + (idx & 1);
+        return *(const bf16x8*)(base + piece * PIECE_BYTES);
+    };
+    // MFMAs of one stage; with `refill`, stage t+1's fragments are read
+    // behind them (its buffer was published by the preceding barrier).
+    auto step = [&](int64_t t, const AFrags& acur, AFrags& anext, BFrags& b, bool refill) {
+        const uint8_t* nbase = stage_ptr(t + 1);
+        if (refill)
+            read_a(t + 1, anext);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+            for (int kc = 0; kc < KCS; ++kc)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        acur.v[kc][fm], b.v[kc][fn], acc[fm][fn], 0, 0, 0);
+            if (refill) {
+#pragma unroll
+                for (int kc = 0; kc < KCS; ++kc)
+                    b.v[kc][fn] = read_b(nbase, kc, fn);
+            }
+        }
+    };
+    // Publishes stage t+1 (its loads done in every wave) and refills the
+    // ring slot that stage t-1 used (its fragments were read a step ago).
+    auto advance = [&](int64_t t) {
+        const int64_t rem = nsteps - 2 - t;
+        wait_stage<PPW, STAGES - 2>((int)(rem < STAGES - 3 ? rem : STAGES - 3));
+        barrier_lds();
+        if (t + STAGES - 1 < nsteps)
+            load_stage(t + STAGES - 1);
+    };
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nsteps)
+            load_stage(s);
+    {
+        const int64_t rem = nsteps - 1;
+        wait_stage<PPW, STAGES - 2>((int)(rem < STAGES - 2 ? rem : STAGES - 2));
+    }
+    barrier_lds();
+    AFrags a0, a1;
+    BFrags b;
+    read_a(0, a0);
+    {
+        const uint8_t* base0 = stage_ptr(0);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int kc = 0; kc < KCS; ++kc)
+                b.v[kc][fn] = read_b(base0, kc, fn);
+    }
+    // Two steps per trip so that both A sets stay in registers; the loop
+    // body has no conditional LDS reads, so the compiler's wait counts stay
+    // exact (a join after a skipped read would make them conservative).
+    int64_t t = 0;
+    for (; t + 2 < nsteps; t += 2) {
+        advance(t);
+        step(t, a0, a1, b, true);
+        advance(t + 1);
+        step(t + 1, a1, a0, b, true);
+    }
+    if (t + 1 < nsteps) {
+        advance(t);
+        step(t, a0, a1, b, true);
+        step(t + 1, a1, a0, b, false);
+    } else {
+        step(t, a0, a1, b, false);
+    }
+
+    // ---- epilogue: lane l holds rows 4*(l/16)+i of column l%16 of each fragment
+    const int c = lane & 15;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int jp = 0; jp < FN / 2; ++jp) {
+            const int64_t pb = pb0 + (wn * FN) / 2 + jp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + wm * S::WTM + fm * 16 + (lane >> 4) * 4 + i;
+                if (row >= M)
+                    continue;
+                uint16_t* orow = out + (int64_t)row * ldo;
+                if (EPI == EPI_SWIGLU) {
+                    const int64_t n = pb * 16 + c;
+                    if (n < ncols_out)
+                        orow[n] = f32_to_bf16(silu(acc[fm][2 * jp][i]) * acc[fm][2 * jp + 1][i]);
+                } else {
+                    const int64_t j = pb * 32 + c;
+                    if (j < ncols_out)
+                        orow[j] = f32_to_bf16(acc[fm][2 * jp][i]);
+                    if (j + 16 < ncols_out)
+                        orow[j + 16] = f32_to_bf16(acc[fm][2 * jp + 1][i]);
+                }
+            }
+        }
+    }
+}
+
+// Host launcher for one configuration.
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI>
+hipError_t launch_wide_cfg(const GemmArgs& g, hipStream_t s, int group_m)
+{
+    using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES>;
+    static bool attr_set = false;   // benign race: every writer stores the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI>,
+            hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    const int tiles_m = (int)ceil_div(g.M, BM);
+    const int tiles_n = (int)ceil_div(ceil_div(g.ncols_out, g.geom.cols_per_pb) * 32, BN);
+    wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI>
+        <<<dim3((unsigned)(tiles_m * tiles_n)), dim3(S::THREADS), S::LDS_BYTES, s>>>(
+            (const uint16_t*)g.a, g.lda, g.geom.K, (int)g.M, (const uint16_t*)g.w, g.geom.nkc,
+            g.geom.npb, (uint16_t*)g.out, g.ldo, g.ncols_out, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
+}  // namespace swg
