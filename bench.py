@@ -33,17 +33,22 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
 F32_VALU_PEAK_TFLOPS = 157.3
 METRIC = "fused SwiGLU MLP: HBM GB/s at M=1 decode; bf16 TFLOP/s at M=4096 prefill"
-KERNEL_SOURCES = ["geometry.h", "device_common.h", "launch.h", "api.hip", "pack.hip",
-                  "skinny.hip", "wide.hip", "wide_kernel.h"]
+# sources each kernel's recorded counters depend on
+COMMON_SOURCES = ["geometry.h", "device_common.h", "launch.h", "api.hip"]
+KERNEL_SOURCES = {
+    "skinny_bf16_kernel": COMMON_SOURCES + ["skinny.hip"],
+    "skinny_f32_kernel": COMMON_SOURCES + ["skinny.hip"],
+    "wide_bf16_kernel": COMMON_SOURCES + ["wide.hip", "wide_kernel.h"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "gemv_gate_up_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -57,7 +62,7 @@ def traffic_from_profile(workload: str, kernel: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("src_sha") != kernel_source_hash() or rec.get("kernel") != kernel:
+    if rec.get("kernel") != kernel or rec.get("src_sha") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -119,30 +124,24 @@ class Runner:
             raise RuntimeError("step failed: %s" % sw.swiglu_status_string(rc))
 
     def time(self, steps: int, warmup: int) -> dict:
-        """Two passes over the same K steps: first back-to-back launches
-        timed by the host clock between synchronisations (the step rate),
-        then the same launches bracketed one by one with HIP events on the
-        launch stream (the kernel duration of one launch)."""
+        """K back-to-back steps between two synchronisations: the host clock
+        gives the step rate, and a pair of HIP events recorded on the launch
+        stream around the same K launches gives the device time per launch."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record(self.stream)
         for i in range(steps):
             self.step(warmup + i)
+        e1.record(self.stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for i in range(steps):
-            evs[i][0].record(self.stream)
-            self.step(warmup + steps + i)
-            evs[i][1].record(self.stream)
-        torch.cuda.synchronize()
-        durs = np.array([a.elapsed_time(b) for a, b in evs])   # ms
         return {"wall_ms_per_step": (t1 - t0) * 1e3 / steps,
-                "event_ms_mean": float(durs.mean()), "event_ms_median": float(np.median(durs)),
-                "event_ms_min": float(durs.min()), "event_ms_max": float(durs.max())}
+                "event_ms_per_launch": e0.elapsed_time(e1) / steps}
 
 
 def dominant_kernel(w: wl.Workload, path: int) -> str:
@@ -155,7 +154,7 @@ def measure(w: wl.Workload, steps: int, warmup: int, copies: int) -> dict:
     r = Runner(w, copies)
     t = r.time(steps, warmup)
     kern = dominant_kernel(w, r.path)
-    per_launch_ms = t["event_ms_mean"]
+    per_launch_ms = t["event_ms_per_launch"]
     single_kernel = (not w.with_down) and (
         r.path == 2 or r.sw.swiglu_workspace_bytes(w.M, w.d, w.dff, w.dtype, 0) == 0)
     res = {"runner": r, "timing": t, "kernel": kern, "path": r.path,
@@ -202,6 +201,31 @@ def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float) -> dict:
             "ms_per_call": round(per_call * 1e3, 2)}
 
 
+def probe() -> int:
+    """Kernels for hardware-counter runs: a plain copy of known size (reads
+    and writes exactly 1 GiB) to calibrate FETCH_SIZE / WRITE_SIZE, then the
+    decode and prefill steps as the bench runs them."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    for name, steps in (("decode8b_m1", 5), ("prefill8b_m4096", 3)):
+        w = wl.WORKLOADS[name]
+        r = Runner(w, 5 if name == "decode8b_m1" else 1)
+        for i in range(steps):
+            r.step(i)
+        torch.cuda.synchronize()
+        del r
+        torch.cuda.empty_cache()
+    log("probe done")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +236,9 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--probe", action="store_true",
+                    help="counter-collection run: a 1 GiB device copy (calibration), then a few "
+                         "steps of the decode and prefill workloads; prints no timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -221,6 +248,8 @@ def main() -> int:
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.probe:
+        return probe()
     w = wl.WORKLOADS[args.workload]
     one_copy = 2 * w.d * w.dff * w.elem_bytes
     copies = max(1, -(-(1 << 30) // one_copy)) if one_copy < (1 << 30) else 1

@@ -183,6 +183,7 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int64_t nsteps = nkc / KCS;
+    static_assert(KCS == 1, "one chunk per stage keeps the step count even");
 
     // Operand fragments in registers.  A fragments are double buffered;
     // each B fragment is refilled from the next stage as soon as the MFMAs
@@ -261,49 +262,62 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
             for (int kc = 0; kc < KCS; ++kc)
                 b.v[kc][fn] = read_b(base0, kc, fn);
     }
-    // Two steps per trip so that both A sets stay in registers; the loop
-    // body has no conditional LDS reads, so the compiler's wait counts stay
-    // exact (a join after a skipped read would make them conservative).
-    int64_t t = 0;
-    for (; t + 2 < nsteps; t += 2) {
+    // Two steps per trip so that both A sets stay in registers.  nsteps is
+    // always even (K is padded to two chunks), so there is no tail: the
+    // last refill reads a stale but in-bounds ring slot whose values are
+    // never used.  No LDS read is conditional, so the compiler's wait
+    // counts stay exact, and no peeled copy of the step raises register
+    // pressure past the loop.
+    for (int64_t t = 0; t < nsteps; t += 2) {
         advance(t);
         step(t, a0, a1, b, true);
         advance(t + 1);
         step(t + 1, a1, a0, b, true);
     }
-    if (t + 1 < nsteps) {
-        advance(t);
-        step(t, a0, a1, b, true);
-        step(t + 1, a1, a0, b, false);
-    } else {
-        step(t, a0, a1, b, false);
-    }
 
-    // ---- epilogue: lane l holds rows 4*(l/16)+i of column l%16 of each fragment
+    // ---- epilogue: lane l holds rows 4*(l/16)+i of column l%16 of each
+    // fragment.  The finished values (silu(gate) * up, or the plain
+    // product) are staged in LDS one wave-row of the tile at a time, then
+    // written to memory as whole rows in 16-byte vectors, so every global
+    // write covers full cache lines.
+    constexpr int OW = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns of the tile
+    constexpr int WOW = OW / WGN;                          // of one wave
+    constexpr int LROW = OW + 8;                           // padded LDS row, elements
+    constexpr int VPR = OW / 8;                            // 16-byte vectors per row
+    static_assert(S::WTM * LROW * 2 <= S::LDS_BYTES, "epilogue staging fits the ring");
+    uint16_t* ep = (uint16_t*)smem;
+    const int64_t col0 = EPI == EPI_SWIGLU ? pb0 * 16 : pb0 * 32;
     const int c = lane & 15;
+#pragma unroll 1
+    for (int pass = 0; pass < WGM; ++pass) {
+        __syncthreads();   // ring reads (first pass) or previous stores (later) are done
+        if (wm == pass) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
+            for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-        for (int jp = 0; jp < FN / 2; ++jp) {
-            const int64_t pb = pb0 + (wn * FN) / 2 + jp;
+                for (int jp = 0; jp < FN / 2; ++jp) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = m0 + wm * S::WTM + fm * 16 + (lane >> 4) * 4 + i;
-                if (row >= M)
-                    continue;
-                uint16_t* orow = out + (int64_t)row * ldo;
-                if (EPI == EPI_SWIGLU) {
-                    const int64_t n = pb * 16 + c;
-                    if (n < ncols_out)
-                        orow[n] = f32_to_bf16(silu(acc[fm][2 * jp][i]) * acc[fm][2 * jp + 1][i]);
-                } else {
-                    const int64_t j = pb * 32 + c;
-                    if (j < ncols_out)
-                        orow[j] = f32_to_bf16(acc[fm][2 * jp][i]);
-                    if (j + 16 < ncols_out)
-                        orow[j + 16] = f32_to_bf16(acc[fm][2 * jp + 1][i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = fm * 16 + (lane >> 4) * 4 + i;
+                        if (EPI == EPI_SWIGLU) {
+                            const float v = silu(acc[fm][2 * jp][i]) * acc[fm][2 * jp + 1][i];
+                            ep[r * LROW + wn * WOW + jp * 16 + c] = f32_to_bf16(v);
+                        } else {
+                            const int cc = wn * WOW + jp * 32 + c;
+                            ep[r * LROW + cc] = f32_to_bf16(acc[fm][2 * jp][i]);
+                            ep[r * LROW + cc + 16] = f32_to_bf16(acc[fm][2 * jp + 1][i]);
+                        }
+                    }
                 }
             }
+        }
+        __syncthreads();
+        for (int v = threadIdx.x; v < S::WTM * VPR; v += S::THREADS) {
+            const int r = v / VPR, cv = v % VPR;
+            const int row = m0 + pass * S::WTM + r;
+            const int64_t col = col0 + cv * 8;
+            if (row < M && col < ncols_out)
+                *(i32x4*)(out + (int64_t)row * ldo + col) = *(const i32x4*)(ep + r * LROW + cv * 8);
         }
     }
 }
