@@ -157,22 +157,23 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         }
     }
 
-    auto load_stage = [&](int64_t t) {
+    // Issues piece j (of this wave's PPW pieces) of stage t into its ring slot.
+    auto load_piece = [&](int64_t t, int j) {
         const uint32_t base = smem_base + (uint32_t)((t % STAGES) * S::STAGE_BYTES);
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) {
-            const int q = wave + j * NW;
-            const uint32_t dst =
-                (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + q * PIECE_BYTES));
-            if (j < APW) {
-                const int64_t k = t * (KCS * 32) + akk[j];
-                const uint32_t o =
-                    k < kvalid ? off[j] + (uint32_t)(t * (KCS * 64)) : OOB_OFFSET;
-                load_lds16(ra, o, dst);
-            } else {
-                load_lds16(rw, off[j] + (uint32_t)(t * (KCS * 2 * PIECE_BYTES)), dst);
-            }
+        const int q = wave + j * NW;
+        const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + q * PIECE_BYTES));
+        if (j < APW) {
+            const int64_t k = t * (KCS * 32) + akk[j];
+            const uint32_t o = k < kvalid ? off[j] + (uint32_t)(t * (KCS * 64)) : OOB_OFFSET;
+            load_lds16(ra, o, dst);
+        } else {
+            load_lds16(rw, off[j] + (uint32_t)(t * (KCS * 2 * PIECE_BYTES)), dst);
         }
+    };
+    auto load_stage = [&](int64_t t) {
+#pragma unroll
+        for (int j = 0; j < PPW; ++j)
+            load_piece(t, j);
     };
 
     f32x4 acc[FM][FN];
@@ -212,9 +213,15 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         return *(const bf16x8*)(base + piece * PIECE_BYTES);
     };
     // MFMAs of one stage; with `refill`, stage t+1's fragments are read
-    // behind them (its buffer was published by the preceding barrier).
+    // behind them (its buffer was published by the preceding barrier).  The
+    // loads of stage t+STAGES-1 are spread over the step, one piece after
+    // each group of MFMAs: the inline asm that issues them bounds the
+    // compiler's scheduling regions, so they stay interleaved with matrix
+    // work instead of arriving in one burst (their ring slot was last read
+    // two steps earlier).
     auto step = [&](int64_t t, const AFrags& acur, AFrags& anext, BFrags& b, bool refill) {
         const uint8_t* nbase = stage_ptr(t + 1);
+        const bool load = t + STAGES - 1 < nsteps;
         if (refill)
             read_a(t + 1, anext);
 #pragma unroll
@@ -230,16 +237,18 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
                 for (int kc = 0; kc < KCS; ++kc)
                     b.v[kc][fn] = read_b(nbase, kc, fn);
             }
+            if (load) {
+#pragma unroll
+                for (int j = fn * PPW / FN; j < (fn + 1) * PPW / FN; ++j)
+                    load_piece(t + STAGES - 1, j);
+            }
         }
     };
-    // Publishes stage t+1 (its loads done in every wave) and refills the
-    // ring slot that stage t-1 used (its fragments were read a step ago).
+    // Publishes stage t+1: its loads are done in every wave.
     auto advance = [&](int64_t t) {
         const int64_t rem = nsteps - 2 - t;
         wait_stage<PPW, STAGES - 2>((int)(rem < STAGES - 3 ? rem : STAGES - 3));
         barrier_lds();
-        if (t + STAGES - 1 < nsteps)
-            load_stage(t + STAGES - 1);
     };
 
 #pragma unroll
