@@ -31,6 +31,7 @@ struct SkinnyPlan {
     int splits;             // K splits across workgroups (1 = epilogue in the same kernel)
     int64_t chunks_per_split;
     int64_t grid_pb;        // pair blocks covered by the grid
+    int pb_per_wg;          // pair blocks per workgroup (bf16: 1 or 2)
     int row_tile;           // rows per workgroup row group (bf16: 16*MT, fp32: 8)
     int64_t row_groups;
 };

@@ -28,7 +28,11 @@ constexpr int SK_WAVES = 4;
 constexpr int SK_THREADS = SK_WAVES * 64;
 
 // ---------------------------------------------------------------- bf16 (MFMA)
-template <int MT, int U, int EPI, bool SPLIT, typename OutT>
+// Each wave covers NPB consecutive pair blocks, so one activation fragment
+// (MT 16-row tiles of x over a 32-K chunk) feeds 2*NPB*MT MFMAs; with 16 or
+// more rows, re-reading that fragment per pair block would cost half as many
+// bytes again as the weights.
+template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT>
 __global__ void __launch_bounds__(SK_THREADS)
 skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                    const i32x4* __restrict__ w, int64_t nkc, int64_t cps,
@@ -37,35 +41,40 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t pb = blockIdx.x;
+    const int64_t pb0 = (int64_t)blockIdx.x * NPB;
     const int s = blockIdx.y;
     const int rbase = blockIdx.z * 16 * MT;
     const int64_t kbeg = (int64_t)s * cps;
     const int64_t kend = kbeg + cps < nkc ? kbeg + cps : nkc;
-    const i32x4* wp = w + pb * nkc * 2 * PIECE_VECS + lane;
+    const i32x4* wp = w + pb0 * nkc * 2 * PIECE_VECS + lane;
 
     // A operand of lane l: row l % 16 of each 16-row tile, k-group l / 16.
     const int arow = lane & 15;
     const int akoff = (lane >> 4) * 8;
 
-    f32x4 accg[MT], accu[MT];
+    f32x4 accg[NPB][MT], accu[NPB][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        accg[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accu[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int p = 0; p < NPB; ++p)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            accg[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accu[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
     for (int64_t kb = kbeg + wave; kb < kend; kb += SK_WAVES * U) {
-        i32x4 wg[U], wu[U];
+        i32x4 wg[NPB][U], wu[NPB][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t kc = kb + SK_WAVES * u;
-            if (kc < kend) {
-                wg[u] = load_nt16(wp + (kc * 2) * PIECE_VECS);
-                wu[u] = load_nt16(wp + (kc * 2 + 1) * PIECE_VECS);
-            } else {
-                wg[u] = i32x4{0, 0, 0, 0};
-                wu[u] = i32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int p = 0; p < NPB; ++p) {
+                if (kc < kend) {
+                    wg[p][u] = load_nt16(wp + (p * nkc * 2 + kc * 2) * PIECE_VECS);
+                    wu[p][u] = load_nt16(wp + (p * nkc * 2 + kc * 2 + 1) * PIECE_VECS);
+                } else {
+                    wg[p][u] = i32x4{0, 0, 0, 0};
+                    wu[p][u] = i32x4{0, 0, 0, 0};
+                }
             }
         }
         i32x4 xa[U][MT];
@@ -84,57 +93,69 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bf16x8 bg = __builtin_bit_cast(bf16x8, wg[u]);
-            const bf16x8 bu = __builtin_bit_cast(bf16x8, wu[u]);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, xa[u][mt]);
-                accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, accg[mt], 0, 0, 0);
-                accu[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, accu[mt], 0, 0, 0);
+            for (int p = 0; p < NPB; ++p) {
+                const bf16x8 bg = __builtin_bit_cast(bf16x8, wg[p][u]);
+                const bf16x8 bu = __builtin_bit_cast(bf16x8, wu[p][u]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, xa[u][mt]);
+                    accg[p][mt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, accg[p][mt], 0, 0, 0);
+                    accu[p][mt] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, accu[p][mt], 0, 0, 0);
+                }
             }
         }
     }
 
-    // Combine the four waves in LDS, in wave order.  MFMA result layout:
-    // lane l holds rows 4*(l/16) + i (i = 0..3) of column l % 16.
+    // Combine the four waves in LDS, in wave order, one pair block at a
+    // time.  MFMA result layout: lane l holds rows 4*(l/16) + i (i = 0..3)
+    // of column l % 16.
     __shared__ float red[SK_WAVES][MT][2][64 * 4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            red[wave][mt][0][lane * 4 + i] = accg[mt][i];
-            red[wave][mt][1][lane * 4 + i] = accu[mt][i];
-        }
-    }
-    __syncthreads();
     const int t = threadIdx.x;
     const int r = t >> 4, c = t & 15;
     const int src = ((r >> 2) * 16 + c) * 4 + (r & 3);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        float g = 0.f, u = 0.f;
+    for (int p = 0; p < NPB; ++p) {
+        const int64_t pb = pb0 + p;
+        if (p > 0)
+            __syncthreads();   // the previous pair block's sums have been read
 #pragma unroll
-        for (int wv = 0; wv < SK_WAVES; ++wv) {
-            g += red[wv][mt][0][src];
-            u += red[wv][mt][1][src];
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                red[wave][mt][0][lane * 4 + i] = accg[p][mt][i];
+                red[wave][mt][1][lane * 4 + i] = accu[p][mt][i];
+            }
         }
-        const int row = rbase + mt * 16 + r;
-        if (row >= M)
-            continue;
-        if (SPLIT) {
-            float* pr = partial + ((int64_t)s * M + row) * npc + pb * 32;
-            pr[c] = g;
-            pr[16 + c] = u;
-        } else if (EPI == EPI_SWIGLU) {
-            const int64_t n = pb * 16 + c;
-            if (n < ncols_out)
-                store_out(out + (int64_t)row * ldo + n, silu(g) * u);
-        } else {
-            const int64_t j = pb * 32 + c;
-            if (j < ncols_out)
-                store_out(out + (int64_t)row * ldo + j, g);
-            if (j + 16 < ncols_out)
-                store_out(out + (int64_t)row * ldo + j + 16, u);
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float g = 0.f, u = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < SK_WAVES; ++wv) {
+                g += red[wv][mt][0][src];
+                u += red[wv][mt][1][src];
+            }
+            const int row = rbase + mt * 16 + r;
+            if (row >= M)
+                continue;
+            if (SPLIT) {
+                float* pr = partial + ((int64_t)s * M + row) * npc + pb * 32;
+                pr[c] = g;
+                pr[16 + c] = u;
+            } else if (EPI == EPI_SWIGLU) {
+                const int64_t n = pb * 16 + c;
+                if (n < ncols_out)
+                    store_out(out + (int64_t)row * ldo + n, silu(g) * u);
+            } else {
+                const int64_t j = pb * 32 + c;
+                if (j < ncols_out)
+                    store_out(out + (int64_t)row * ldo + j, g);
+                if (j + 16 < ncols_out)
+                    store_out(out + (int64_t)row * ldo + j + 16, u);
+            }
         }
     }
 }
@@ -281,6 +302,12 @@ static int bf16_row_tiles(int64_t M) {
     return (int)(mt > 4 ? 4 : (mt < 1 ? 1 : mt));
 }
 
+// Pair blocks per wave of the bf16 kernel: two once x's fragment is as large
+// as a weight piece (more than 8 rows), one otherwise.
+static int bf16_pair_blocks(int64_t M) {
+    return M > 8 ? 2 : 1;
+}
+
 static int f32_row_tile(int64_t M) {
     return M >= 8 ? 8 : (M > 2 ? 4 : (M == 2 ? 2 : 1));
 }
@@ -289,8 +316,12 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
 {
     SkinnyPlan p;
     p.grid_pb = ceil_div(g.ncols_out, g.geom.cols_per_pb);
+    p.pb_per_wg = g.dt == DT_BF16 ? bf16_pair_blocks(g.M) : 1;
     p.row_tile = g.dt == DT_BF16 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M);
     p.row_groups = ceil_div(g.M, p.row_tile);
+    // Split K only when there are too few pair blocks (units of weight
+    // streaming) to keep every CU busy; two pair blocks per workgroup are
+    // still two units of work.
     const int64_t base = p.grid_pb * p.row_groups;
     const int64_t target = 2 * (int64_t)num_cus;
     const int64_t min_chunks = 8;
@@ -309,32 +340,44 @@ size_t skinny_partial_bytes(const GemmArgs& g, const SkinnyPlan& p)
     return (size_t)p.splits * (size_t)g.M * (size_t)(g.geom.npb * 32) * sizeof(float);
 }
 
-template <int MT, int U, int EPI, bool SPLIT, typename OutT>
+template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT>
 static void go_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
-    dim3 grid((unsigned)p.grid_pb, (unsigned)p.splits, (unsigned)p.row_groups);
-    skinny_bf16_kernel<MT, U, EPI, SPLIT, OutT><<<grid, dim3(SK_THREADS), 0, s>>>(
+    // With two pair blocks per workgroup and an odd count, the last
+    // workgroup's second pair block is padding (zero weights, never stored):
+    // the packed buffer holds a multiple of 8 pair blocks.
+    dim3 grid((unsigned)ceil_div(p.grid_pb, NPB), (unsigned)p.splits, (unsigned)p.row_groups);
+    skinny_bf16_kernel<MT, U, NPB, EPI, SPLIT, OutT><<<grid, dim3(SK_THREADS), 0, s>>>(
         (const uint16_t*)g.a, g.lda, g.geom.K, (const i32x4*)g.w, g.geom.nkc, p.chunks_per_split,
         (OutT*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M);
 }
 
-template <int MT, int U, int EPI>
+template <int MT, int U, int NPB, int EPI>
 static void pick_split_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     if (p.splits > 1)
-        go_bf16<MT, U, EPI, true, uint16_t>(g, p, partial, s);
+        go_bf16<MT, U, NPB, EPI, true, uint16_t>(g, p, partial, s);
     else
-        go_bf16<MT, U, EPI, false, uint16_t>(g, p, partial, s);
+        go_bf16<MT, U, NPB, EPI, false, uint16_t>(g, p, partial, s);
 }
 
+// Loads in flight per lane: 2*NPB*U weight pieces plus U*MT activation
+// fragments (measured on the 8B- and 72B-class decode shapes).
 template <int EPI>
 static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     switch (p.row_tile / 16) {
-    case 1: pick_split_bf16<1, 8, EPI>(g, p, partial, s); break;
-    case 2: pick_split_bf16<2, 8, EPI>(g, p, partial, s); break;
-    case 3: pick_split_bf16<3, 4, EPI>(g, p, partial, s); break;
-    default: pick_split_bf16<4, 4, EPI>(g, p, partial, s); break;
+    case 1:
+        if (p.pb_per_wg == 2)
+            pick_split_bf16<1, 4, 2, EPI>(g, p, partial, s);
+        else if (g.M > 4)
+            pick_split_bf16<1, 4, 1, EPI>(g, p, partial, s);
+        else
+            pick_split_bf16<1, 8, 1, EPI>(g, p, partial, s);
+        break;
+    case 2: pick_split_bf16<2, 4, 2, EPI>(g, p, partial, s); break;
+    case 3: pick_split_bf16<3, 2, 2, EPI>(g, p, partial, s); break;
+    default: pick_split_bf16<4, 2, 2, EPI>(g, p, partial, s); break;
     }
 }
 
