@@ -4,10 +4,10 @@
 
 namespace swg {
 
-// 256 x 256 fused-column tile, 8 waves (2 per SIMD) of 128 x 64, stages of
+// 256 x 256 fused-column tile, 8 waves (2 per SIMD) of 64 x 128, stages of
 // one 32-K chunk, four stages in the LDS ring (up to three in flight).
 struct WideCfg {
-    static constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, KCS = 1, STAGES = 4;
+    static constexpr int BM = 256, BN = 256, WGM = 4, WGN = 2, KCS = 1, STAGES = 4;
     static constexpr int GROUP_M = 8;
 };
 

@@ -58,14 +58,16 @@ __device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t num_bytes) 
     return r;
 }
 
-// 16 bytes per lane, global -> LDS at lds_base + 16 * lane, bypassing VGPRs.
+// 16 bytes per lane, global -> LDS at lds_base + 16 * lane, bypassing VGPRs;
+// the address is base + voffset (per lane) + soffset (per wave, the K step).
 // Issued through inline asm so that the compiler does not add a blanket
-// vmcnt(0) before LDS reads; completion is awaited with wait_vmcnt.
-__device__ __forceinline__ void load_lds16(const i32x4& srd, uint32_t voffset,
+// vmcnt(0) before LDS reads; completion is awaited with wait_vmcnt.  A lane
+// whose voffset alone is past num_records reads zero whatever soffset is.
+__device__ __forceinline__ void load_lds16(const i32x4& srd, uint32_t voffset, uint32_t soffset,
                                            uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "v"(voffset), "s"(srd), "s"(lds_base)
+                 : "v"(voffset), "s"(srd), "s"(soffset), "s"(lds_base)
                  : "memory", "m0");
 }
 
@@ -99,7 +101,7 @@ __device__ __forceinline__ void wait_stage(int ahead) {
     wait_vmcnt<0>();
 }
 
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI>
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL>
 __global__ void __launch_bounds__(WGM * WGN * 64, 1)
 wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, int M,
                  const uint16_t* __restrict__ w, int64_t nkc, int64_t npb,
@@ -157,17 +159,22 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         }
     }
 
-    // Issues piece j (of this wave's PPW pieces) of stage t into its ring slot.
+    // Issues piece j (of this wave's PPW pieces) of stage t into its ring
+    // slot.  The K step advances through the scalar offset; only when K is
+    // not a multiple of the stage depth (KTAIL) do A lanes past K take an
+    // out-of-range offset so that they read zero.
     auto load_piece = [&](int64_t t, int j) {
         const uint32_t base = smem_base + (uint32_t)((t % STAGES) * S::STAGE_BYTES);
         const int q = wave + j * NW;
         const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + q * PIECE_BYTES));
         if (j < APW) {
-            const int64_t k = t * (KCS * 32) + akk[j];
-            const uint32_t o = k < kvalid ? off[j] + (uint32_t)(t * (KCS * 64)) : OOB_OFFSET;
-            load_lds16(ra, o, dst);
+            const uint32_t so = (uint32_t)(t * (KCS * 64));
+            uint32_t o = off[j];
+            if (KTAIL && t * (KCS * 32) + akk[j] >= kvalid)
+                o = OOB_OFFSET;
+            load_lds16(ra, o, so, dst);
         } else {
-            load_lds16(rw, off[j] + (uint32_t)(t * (KCS * 2 * PIECE_BYTES)), dst);
+            load_lds16(rw, off[j], (uint32_t)(t * (KCS * 2 * PIECE_BYTES)), dst);
         }
     };
     auto load_stage = [&](int64_t t) {
@@ -332,14 +339,14 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
 }
 
 // Host launcher for one configuration.
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI>
-hipError_t launch_wide_cfg(const GemmArgs& g, hipStream_t s, int group_m)
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL>
+static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m)
 {
     using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES>;
     static bool attr_set = false;   // benign race: every writer stores the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI>,
+            (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL>,
             hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
         if (e != hipSuccess)
             return e;
@@ -347,11 +354,19 @@ hipError_t launch_wide_cfg(const GemmArgs& g, hipStream_t s, int group_m)
     }
     const int tiles_m = (int)ceil_div(g.M, BM);
     const int tiles_n = (int)ceil_div(ceil_div(g.ncols_out, g.geom.cols_per_pb) * 32, BN);
-    wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI>
+    wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL>
         <<<dim3((unsigned)(tiles_m * tiles_n)), dim3(S::THREADS), S::LDS_BYTES, s>>>(
             (const uint16_t*)g.a, g.lda, g.geom.K, (int)g.M, (const uint16_t*)g.w, g.geom.nkc,
             g.geom.npb, (uint16_t*)g.out, g.ldo, g.ncols_out, tiles_m, tiles_n, group_m);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI>
+hipError_t launch_wide_cfg(const GemmArgs& g, hipStream_t s, int group_m)
+{
+    if (g.geom.K % (KCS * 32) == 0)
+        return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false>(g, s, group_m);
+    return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, true>(g, s, group_m);
 }
 
 }  // namespace swg
