@@ -70,7 +70,7 @@ def traffic_from_profile(workload: str, kernel: str):
 class Runner:
     """Device buffers and the C-ABI call for one workload."""
 
-    def __init__(self, w: wl.Workload, copies: int):
+    def __init__(self, w: wl.Workload, copies: int, path: int = 0):
         import torch
         import gemv_gate_up_amd as sw
         self.torch, self.sw, self.w = torch, sw, w
@@ -99,13 +99,16 @@ class Runner:
             self.wdps = [wdp] + [wdp.clone() for _ in range(copies - 1)]
         ncols = w.d if w.with_down else w.dff
         self.out = torch.empty((w.M, ncols), dtype=tdt, device="cuda")
-        self.ws_bytes = sw.swiglu_workspace_bytes(w.M, w.d, w.dff, w.dtype, int(w.with_down))
+        self.req_path = path
+        self.ws_bytes = sw.swiglu_workspace_bytes_ex(w.M, w.d, w.dff, w.dtype, int(w.with_down), path)
+        if self.ws_bytes < 0:
+            raise RuntimeError("path %d: %s" % (path, sw.swiglu_status_string(self.ws_bytes)))
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream()
         self.sh = self.stream.cuda_stream
         self.copies = copies
-        self.path = sw.swiglu_select_path(w.M, w.d, w.dff, w.dtype)
+        self.path = path or sw.swiglu_select_path(w.M, w.d, w.dff, w.dtype)
         # raw pointers once, so a step is a single foreign call
         self.args = [(self.x.data_ptr(), self.wps[i].data_ptr(),
                       self.wdps[i].data_ptr() if self.wdps[i] is not None else None)
@@ -114,7 +117,14 @@ class Runner:
     def step(self, i: int) -> None:
         w, sw = self.w, self.sw
         xp, wpp, wdpp = self.args[i % self.copies]
-        if w.with_down:
+        if self.req_path and w.with_down:
+            rc = sw._lib.mlp_forward_ex(xp, wpp, wdpp, self.out.data_ptr(), w.M, w.d, w.dff,
+                                        w.dtype, self.ws.data_ptr(), self.ws_bytes, self.sh,
+                                        self.req_path)
+        elif self.req_path:
+            rc = sw._lib.swiglu_up_ex(xp, wpp, self.out.data_ptr(), w.M, w.d, w.dff, w.dtype,
+                                      self.ws.data_ptr(), self.ws_bytes, self.sh, self.req_path)
+        elif w.with_down:
             rc = sw._lib.mlp_forward(xp, wpp, wdpp, self.out.data_ptr(), w.M, w.d, w.dff, w.dtype,
                                      self.ws.data_ptr(), self.ws_bytes, self.sh)
         else:
@@ -144,19 +154,23 @@ class Runner:
                 "event_ms_per_launch": e0.elapsed_time(e1) / steps}
 
 
+PATHS = {"auto": 0, "skinny": 1, "wide": 2, "phased": 3}
+PATH_NAMES = {1: "skinny", 2: "wide", 3: "wide-phased"}
+
+
 def dominant_kernel(w: wl.Workload, path: int) -> str:
-    if path == 2:
+    if path in (2, 3):
         return "wide_bf16_kernel"
     return "skinny_bf16_kernel" if w.dtype == wl.BF16 else "skinny_f32_kernel"
 
 
-def measure(w: wl.Workload, steps: int, warmup: int, copies: int) -> dict:
-    r = Runner(w, copies)
+def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0) -> dict:
+    r = Runner(w, copies, path)
     t = r.time(steps, warmup)
     kern = dominant_kernel(w, r.path)
     per_launch_ms = t["event_ms_per_launch"]
     single_kernel = (not w.with_down) and (
-        r.path == 2 or r.sw.swiglu_workspace_bytes(w.M, w.d, w.dff, w.dtype, 0) == 0)
+        r.path in (2, 3) or r.sw.swiglu_workspace_bytes(w.M, w.d, w.dff, w.dtype, 0) == 0)
     res = {"runner": r, "timing": t, "kernel": kern, "path": r.path,
            "single_kernel_step": single_kernel}
     bytes_alg = w.algorithmic_bytes()
@@ -171,7 +185,8 @@ def measure(w: wl.Workload, steps: int, warmup: int, copies: int) -> dict:
         res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1),
                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-    res["roofline"]["traffic"] = traffic_from_profile(w.name, kern)
+    # recorded counters are for the dispatcher's own path
+    res["roofline"]["traffic"] = traffic_from_profile(w.name, kern) if not path else None
     res["roofline"]["kernel"] = kern
     res["roofline"]["kernel_ms"] = round(per_launch_ms, 5)
     return res
@@ -233,7 +248,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode8b_m1", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--path", default="auto", choices=sorted(PATHS),
+                    help="force a kernel path for the main workload (default: the dispatcher's)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--probe", action="store_true",
@@ -254,7 +272,7 @@ def main() -> int:
     one_copy = 2 * w.d * w.dff * w.elem_bytes
     copies = max(1, -(-(1 << 30) // one_copy)) if one_copy < (1 << 30) else 1
     log("workload %s: %s, %d weight copies" % (w.name, w, copies))
-    m = measure(w, args.steps, args.warmup, copies)
+    m = measure(w, args.steps, args.warmup, copies, PATHS[args.path])
     t = m["timing"]
     value_bytes = w.algorithmic_bytes() / (t["wall_ms_per_step"] * 1e-3) / 1e9
     rec = {
@@ -271,7 +289,7 @@ def main() -> int:
         "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights, bf16 RNE)",
         "config": {"workload": w.name, "M": w.M, "d": w.d, "dff": w.dff,
-                   "with_down": w.with_down, "path": "skinny" if m["path"] == 1 else "wide",
+                   "with_down": w.with_down, "path": PATH_NAMES[m["path"]],
                    "weight_copies": copies, "algorithmic_bytes": w.algorithmic_bytes(),
                    "algorithmic_flops": w.algorithmic_flops()},
         "roofline": m["roofline"],
@@ -283,13 +301,13 @@ def main() -> int:
     torch.cuda.empty_cache()
     if not args.no_prefill and w.name != "prefill8b_m4096":
         p = wl.WORKLOADS["prefill8b_m4096"]
-        mp = measure(p, args.prefill_steps, 3, 1)
+        mp = measure(p, args.prefill_steps, args.prefill_warmup, 1)
         tp = mp["timing"]
         rec["prefill"] = {
             "workload": p.name, "M": p.M, "d": p.d, "dff": p.dff,
             "value": round(p.algorithmic_flops() / (tp["wall_ms_per_step"] * 1e-3) / 1e12, 1),
             "unit": "TFLOP/s", "ms_per_step": round(tp["wall_ms_per_step"], 4),
-            "steps": args.prefill_steps, "warmup": 3, "roofline": mp["roofline"],
+            "steps": args.prefill_steps, "warmup": args.prefill_warmup, "roofline": mp["roofline"],
             "timing_ms": {k: round(v, 5) for k, v in tp.items()},
         }
     print(json.dumps(rec), flush=True)

@@ -33,6 +33,7 @@ SWIGLU_ERR_HIP = -5
 SWIGLU_PATH_AUTO = 0
 SWIGLU_PATH_SKINNY = 1
 SWIGLU_PATH_WIDE = 2
+SWIGLU_PATH_WIDE_PHASED = 3
 
 
 class SwigluError(RuntimeError):

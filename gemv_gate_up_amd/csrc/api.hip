@@ -40,7 +40,8 @@ int check_sizes(int64_t M, int64_t d, int64_t dff, int dtype)
 
 int check_path(int path)
 {
-    return (path == SWIGLU_PATH_AUTO || path == SWIGLU_PATH_SKINNY || path == SWIGLU_PATH_WIDE)
+    return (path == SWIGLU_PATH_AUTO || path == SWIGLU_PATH_SKINNY || path == SWIGLU_PATH_WIDE ||
+            path == SWIGLU_PATH_WIDE_PHASED)
                ? SWIGLU_OK
                : SWIGLU_ERR_UNSUPPORTED;
 }
@@ -74,9 +75,15 @@ GemmArgs down_args(int64_t M, int64_t d, int64_t dff, int dt)
     return g;
 }
 
-// Resolves the path of one product: SKINNY or WIDE, or an error.
+// Resolves the path of one product: SKINNY, WIDE or WIDE_PHASED, or an
+// error.  The two-pass schedule exists for the gate/up pair only; a plain
+// product asked for it takes the one-pass kernel.
 int resolve_path(const GemmArgs& g, int path)
 {
+    if (path == SWIGLU_PATH_WIDE_PHASED && g.epi == EPI_PLAIN)
+        path = SWIGLU_PATH_WIDE;
+    if (path == SWIGLU_PATH_WIDE_PHASED)
+        return wide_supported(g) ? SWIGLU_PATH_WIDE_PHASED : SWIGLU_ERR_UNSUPPORTED;
     if (path == SWIGLU_PATH_WIDE)
         return wide_supported(g) ? SWIGLU_PATH_WIDE : SWIGLU_ERR_UNSUPPORTED;
     if (path == SWIGLU_PATH_SKINNY)
@@ -124,6 +131,8 @@ int run(const GemmArgs& g, int path, void* partial, hipStream_t s)
     hipError_t e;
     if (path == SWIGLU_PATH_WIDE)
         e = launch_wide(g, s);
+    else if (path == SWIGLU_PATH_WIDE_PHASED)
+        e = launch_wide_phased(g, s);
     else
         e = launch_skinny(g, plan_skinny(g, TARGET_CUS), (float*)partial, s);
     return e == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_HIP;

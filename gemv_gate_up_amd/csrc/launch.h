@@ -44,6 +44,8 @@ hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial,
 
 // Wide path (wide.hip): bf16 MFMA GEMM with LDS double buffering.
 hipError_t launch_wide(const GemmArgs& g, hipStream_t s);
+// Two-pass (gate K loop, then up K loop) schedule; gate/up products only.
+hipError_t launch_wide_phased(const GemmArgs& g, hipStream_t s);
 int wide_supported(const GemmArgs& g);
 
 }  // namespace swg

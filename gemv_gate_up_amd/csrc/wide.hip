@@ -11,6 +11,15 @@ struct WideCfg {
     static constexpr int GROUP_M = 8;
 };
 
+// The two-pass schedule keeps silu(gate) in registers beside the up
+// accumulators, so at the same register budget its tile holds half as many
+// output columns: 256 rows x 128 outputs, 8 waves of 64 x 64.
+struct WidePhasedCfg {
+    static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 2, KCS = 1, STAGES = 4;
+    static constexpr int GROUP_M = 8;
+};
+static_assert(WideCfg::BN / 32 == WidePhasedCfg::BN / 16, "both schedules tile 8 pair blocks");
+
 int wide_supported(const GemmArgs& g)
 {
     // bf16 only; the A region of one tile must stay under 2 GB of byte
@@ -26,6 +35,15 @@ hipError_t launch_wide(const GemmArgs& g, hipStream_t s)
         return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_SWIGLU>(
             g, s, C::GROUP_M);
     return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_PLAIN>(
+        g, s, C::GROUP_M);
+}
+
+hipError_t launch_wide_phased(const GemmArgs& g, hipStream_t s)
+{
+    using C = WidePhasedCfg;
+    if (g.epi != EPI_SWIGLU)
+        return hipErrorInvalidValue;
+    return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_SWIGLU, true>(
         g, s, C::GROUP_M);
 }
 

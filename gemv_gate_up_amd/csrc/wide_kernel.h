@@ -20,6 +20,15 @@
 //   * tiles are remapped so each XCD (own L2) works through a compact group
 //     of tiles that share A row panels and B column panels.
 // The down projection runs through the same kernel with a plain epilogue.
+//
+// PHASED selects the other schedule of that paper (Kernel-1): the tile's
+// accumulators hold gate columns only; the K loop runs once over the gate
+// halves of the tile's pair blocks, silu is applied to the finished gate
+// tile in registers while the first up stages are already in flight, and a
+// second K loop over the up halves (re-reading A) ends in the product.  BN
+// then counts output columns, and the result is bit-identical to the
+// interleaved schedule: every accumulator sums the same MFMAs in the same
+// K order.
 #pragma once
 #include "device_common.h"
 #include "launch.h"
@@ -71,22 +80,23 @@ __device__ __forceinline__ void load_lds16(const i32x4& srd, uint32_t voffset, u
                  : "memory", "m0");
 }
 
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES>
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, bool PHASED = false>
 struct WideShape {
     static constexpr int NW = WGM * WGN;
     static constexpr int THREADS = NW * 64;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
-    static constexpr int PB_TILE = BN / 32;
+    static constexpr int HALVES = PHASED ? 1 : 2;         // B halves loaded per stage
+    static constexpr int PB_TILE = BN / (16 * HALVES);
     static constexpr int A_PIECES = (BM / 16) * KCS;      // [row block][chunk]
-    static constexpr int B_PIECES = PB_TILE * KCS * 2;    // [pair block][chunk][half]
+    static constexpr int B_PIECES = PB_TILE * KCS * HALVES;   // [pair block][chunk][half]
     static constexpr int PIECES = A_PIECES + B_PIECES;
     static constexpr int PPW = PIECES / NW;               // loads per wave per stage
     static constexpr int APW = A_PIECES / NW;
     static constexpr int STAGE_BYTES = PIECES * PIECE_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static_assert(PIECES % NW == 0 && A_PIECES % NW == 0, "pieces must split evenly");
-    static_assert(FN % 2 == 0, "a wave tile holds whole pair blocks");
+    static_assert(PHASED || FN % 2 == 0, "a wave tile holds whole pair blocks");
     static_assert(STAGES >= 3, "stage t+1 must be in flight before step t starts");
     static_assert((STAGES - 2) * PPW < 64, "vmcnt budget");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -101,16 +111,17 @@ __device__ __forceinline__ void wait_stage(int ahead) {
     wait_vmcnt<0>();
 }
 
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL>
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED>
 __global__ void __launch_bounds__(WGM * WGN * 64, 1)
 wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, int M,
                  const uint16_t* __restrict__ w, int64_t nkc, int64_t npb,
                  uint16_t* __restrict__ out, int64_t ldo, int64_t ncols_out,
                  int tiles_m, int tiles_n, int group_m)
 {
-    using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES>;
+    using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
     constexpr int FM = S::FM, FN = S::FN, PPW = S::PPW, APW = S::APW, NW = S::NW;
     constexpr int A_PIECES = S::A_PIECES;
+    static_assert(!PHASED || EPI == EPI_SWIGLU, "the phased schedule is for the gate/up pair");
 
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -154,10 +165,16 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
             off[j] = (uint32_t)(((int64_t)row * lda + kk) * 2);
         } else {
             const int qb = q - A_PIECES;
-            const int pbl = qb / (KCS * 2), kc = (qb / 2) % KCS, half = qb & 1;
+            const int pbl = qb / (KCS * S::HALVES), kc = (qb / S::HALVES) % KCS;
+            const int half = PHASED ? 0 : qb & 1;
             off[j] = (uint32_t)(((int64_t)(pbl * nkc + kc) * 2 + half) * PIECE_BYTES + lane * 16);
         }
     }
+
+    // K steps of one pass; the phased schedule makes two passes, the
+    // second over the up halves.
+    const int64_t kpass = nkc / KCS;
+    const int64_t nsteps = PHASED ? 2 * kpass : kpass;
 
     // Issues piece j (of this wave's PPW pieces) of stage t into its ring
     // slot.  The K step advances through the scalar offset; only when K is
@@ -167,14 +184,17 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         const uint32_t base = smem_base + (uint32_t)((t % STAGES) * S::STAGE_BYTES);
         const int q = wave + j * NW;
         const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + q * PIECE_BYTES));
+        const bool up_pass = PHASED && t >= kpass;
+        const int64_t tk = up_pass ? t - kpass : t;
         if (j < APW) {
-            const uint32_t so = (uint32_t)(t * (KCS * 64));
+            const uint32_t so = (uint32_t)(tk * (KCS * 64));
             uint32_t o = off[j];
-            if (KTAIL && t * (KCS * 32) + akk[j] >= kvalid)
+            if (KTAIL && tk * (KCS * 32) + akk[j] >= kvalid)
                 o = OOB_OFFSET;
             load_lds16(ra, o, so, dst);
         } else {
-            load_lds16(rw, off[j], (uint32_t)(t * (KCS * 2 * PIECE_BYTES)), dst);
+            const uint32_t so = (uint32_t)(tk * (KCS * 2 * PIECE_BYTES)) + (up_pass ? PIECE_BYTES : 0);
+            load_lds16(rw, off[j], so, dst);
         }
     };
     auto load_stage = [&](int64_t t) {
@@ -190,8 +210,7 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         for (int j = 0; j < FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t nsteps = nkc / KCS;
-    static_assert(KCS == 1, "one chunk per stage keeps the step count even");
+    static_assert(KCS == 1, "one chunk per stage keeps the step count of a pass even");
 
     // Operand fragments in registers.  A fragments are double buffered;
     // each B fragment is refilled from the next stage as soon as the MFMAs
@@ -216,7 +235,8 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     };
     auto read_b = [&](const uint8_t* base, int kc, int fn) {
         const int idx = wn * FN + fn;
-        const int piece = A_PIECES + ((idx >> 1) * KCS + kc) * 2 + (idx & 1);
+        const int piece = PHASED ? A_PIECES + idx * KCS + kc
+                                 : A_PIECES + ((idx >> 1) * KCS + kc) * 2 + (idx & 1);
         return *(const bf16x8*)(base + piece * PIECE_BYTES);
     };
     // MFMAs of one stage; with `refill`, stage t+1's fragments are read
@@ -278,17 +298,37 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
             for (int kc = 0; kc < KCS; ++kc)
                 b.v[kc][fn] = read_b(base0, kc, fn);
     }
-    // Two steps per trip so that both A sets stay in registers.  nsteps is
-    // always even (K is padded to two chunks), so there is no tail: the
-    // last refill reads a stale but in-bounds ring slot whose values are
-    // never used.  No LDS read is conditional, so the compiler's wait
-    // counts stay exact, and no peeled copy of the step raises register
-    // pressure past the loop.
-    for (int64_t t = 0; t < nsteps; t += 2) {
+    // Two steps per trip so that both A sets stay in registers.  A pass
+    // always has an even step count (K is padded to two chunks), so there
+    // is no tail: the last refill reads a stale but in-bounds ring slot
+    // whose values are never used.  No LDS read is conditional, so the
+    // compiler's wait counts stay exact, and no peeled copy of the step
+    // raises register pressure past the loop.
+    for (int64_t t = 0; t < kpass; t += 2) {
         advance(t);
         step(t, a0, a1, b, true);
         advance(t + 1);
         step(t + 1, a1, a0, b, true);
+    }
+    // Phased: the gate tile is finished; keep silu(gate) and run the up pass
+    // (its first stages were issued during the gate pass).
+    f32x4 gs[PHASED ? FM : 1][PHASED ? FN : 1];
+    if constexpr (PHASED) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gs[i][j][e] = silu(acc[i][j][e]);
+                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        for (int64_t t = kpass; t < nsteps; t += 2) {
+            advance(t);
+            step(t, a0, a1, b, true);
+            advance(t + 1);
+            step(t + 1, a1, a0, b, true);
+        }
     }
 
     // ---- epilogue: lane l holds rows 4*(l/16)+i of column l%16 of each
@@ -296,13 +336,14 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     // product) are staged in LDS one wave-row of the tile at a time, then
     // written to memory as whole rows in 16-byte vectors, so every global
     // write covers full cache lines.
-    constexpr int OW = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns of the tile
+    constexpr int OW = EPI == EPI_SWIGLU && !PHASED ? BN / 2 : BN;   // output columns of the tile
     constexpr int WOW = OW / WGN;                          // of one wave
     constexpr int LROW = OW + 8;                           // padded LDS row, elements
     constexpr int VPR = OW / 8;                            // 16-byte vectors per row
     static_assert(S::WTM * LROW * 2 <= S::LDS_BYTES, "epilogue staging fits the ring");
     uint16_t* ep = (uint16_t*)smem;
     const int64_t col0 = EPI == EPI_SWIGLU ? pb0 * 16 : pb0 * 32;
+    (void)gs;
     const int c = lane & 15;
 #pragma unroll 1
     for (int pass = 0; pass < WGM; ++pass) {
@@ -310,6 +351,17 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         if (wm == pass) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
+                if constexpr (PHASED) {
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = fm * 16 + (lane >> 4) * 4 + i;
+                            ep[r * LROW + wn * WOW + fn * 16 + c] =
+                                f32_to_bf16(gs[fm][fn][i] * acc[fm][fn][i]);
+                        }
+                    continue;
+                }
 #pragma unroll
                 for (int jp = 0; jp < FN / 2; ++jp) {
 #pragma unroll
@@ -339,34 +391,34 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
 }
 
 // Host launcher for one configuration.
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL>
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED>
 static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m)
 {
-    using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES>;
+    using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
     static bool attr_set = false;   // benign race: every writer stores the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(
-            (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL>,
+            (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED>,
             hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
         if (e != hipSuccess)
             return e;
         attr_set = true;
     }
     const int tiles_m = (int)ceil_div(g.M, BM);
-    const int tiles_n = (int)ceil_div(ceil_div(g.ncols_out, g.geom.cols_per_pb) * 32, BN);
-    wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL>
+    const int tiles_n = (int)ceil_div(ceil_div(g.ncols_out, g.geom.cols_per_pb), S::PB_TILE);
+    wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED>
         <<<dim3((unsigned)(tiles_m * tiles_n)), dim3(S::THREADS), S::LDS_BYTES, s>>>(
             (const uint16_t*)g.a, g.lda, g.geom.K, (int)g.M, (const uint16_t*)g.w, g.geom.nkc,
             g.geom.npb, (uint16_t*)g.out, g.ldo, g.ncols_out, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI>
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED = false>
 hipError_t launch_wide_cfg(const GemmArgs& g, hipStream_t s, int group_m)
 {
     if (g.geom.K % (KCS * 32) == 0)
-        return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false>(g, s, group_m);
-    return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, true>(g, s, group_m);
+        return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED>(g, s, group_m);
+    return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, true, PHASED>(g, s, group_m);
 }
 
 }  // namespace swg

@@ -64,7 +64,16 @@ typedef enum swiglu_status {
 typedef enum swiglu_path {
     SWIGLU_PATH_AUTO = 0,      /* dispatcher: few rows -> skinny, many rows -> wide */
     SWIGLU_PATH_SKINNY = 1,    /* split-over-weights kernels (any M, any dtype) */
-    SWIGLU_PATH_WIDE = 2       /* bf16 MFMA GEMM with LDS double buffering */
+    SWIGLU_PATH_WIDE = 2,      /* bf16 MFMA GEMM with LDS double buffering */
+    /* bf16 MFMA GEMM, two-pass schedule: per output tile a K loop over the
+     * gate columns, silu in registers, then a K loop over the up columns
+     * (Kernel-1 of "Tile-Level Activation Overlap for Efficient LLM
+     * Inference", section on its two kernel designs).  Results are
+     * bit-identical to SWIGLU_PATH_WIDE; the dispatcher never picks it
+     * because it is slower on MI355X at every measured shape.  In
+     * mlp_forward_ex it applies to the gate/up product; the down product
+     * then takes SWIGLU_PATH_WIDE. */
+    SWIGLU_PATH_WIDE_PHASED = 3
 } swiglu_path_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -125,8 +134,8 @@ int swiglu_up(const void *x, const void *Wpacked, void *out,
               int64_t M, int64_t d, int64_t dff, int dtype,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* swiglu_up with a forced path (swiglu_path_t); WIDE with fp32 returns
- * SWIGLU_ERR_UNSUPPORTED. */
+/* swiglu_up with a forced path (swiglu_path_t); WIDE or WIDE_PHASED with
+ * fp32 returns SWIGLU_ERR_UNSUPPORTED. */
 int swiglu_up_ex(const void *x, const void *Wpacked, void *out,
                  int64_t M, int64_t d, int64_t dff, int dtype,
                  void *workspace, size_t workspace_bytes, hipStream_t stream, int path);

@@ -100,8 +100,16 @@ def test_workspace_too_small_is_rejected():
 def test_forced_paths():
     rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, F32, None, 0, 0, sw.SWIGLU_PATH_WIDE)
     assert rc == sw.SWIGLU_ERR_UNSUPPORTED
-    rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, BF16, None, 0, 0, 3)
+    rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, F32, None, 0, 0,
+                         sw.SWIGLU_PATH_WIDE_PHASED)
     assert rc == sw.SWIGLU_ERR_UNSUPPORTED
+    rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, BF16, None, 0, 0, 4)
+    assert rc == sw.SWIGLU_ERR_UNSUPPORTED
+    # the two-pass schedule needs no workspace, with or without the down product
+    assert sw.swiglu_workspace_bytes_ex(4096, 4096, 14336, BF16, 0,
+                                        sw.SWIGLU_PATH_WIDE_PHASED) == 0
+    assert sw.swiglu_workspace_bytes_ex(96, 512, 1408, BF16, 1, sw.SWIGLU_PATH_WIDE_PHASED) == \
+        sw.swiglu_workspace_bytes_ex(96, 512, 1408, BF16, 1, sw.SWIGLU_PATH_WIDE)
 
 
 def test_workloads_shapes_are_supported():

@@ -16,6 +16,7 @@ from swiglu_testlib import (TOL, assert_close, compare, dev, host, pack, run_mlp
 pytestmark = pytest.mark.gpu
 
 SKINNY, WIDE, AUTO = sw.SWIGLU_PATH_SKINNY, sw.SWIGLU_PATH_WIDE, sw.SWIGLU_PATH_AUTO
+PHASED = sw.SWIGLU_PATH_WIDE_PHASED
 BF16, F32 = wl.BF16, wl.F32
 
 
@@ -77,7 +78,7 @@ BF16_UP_SHAPES = [
 
 
 @pytest.mark.parametrize("shape", BF16_UP_SHAPES)
-@pytest.mark.parametrize("path", [AUTO, SKINNY, WIDE])
+@pytest.mark.parametrize("path", [AUTO, SKINNY, WIDE, PHASED])
 def test_up_bf16_random(shape, path):
     M, d, dff = shape
     say("up bf16", shape, "path", path)
@@ -107,10 +108,10 @@ MLP_SHAPES = [(1, 256, 512, BF16), (7, 136, 392, BF16), (64, 896, 4864, BF16),
 
 
 @pytest.mark.parametrize("shape", MLP_SHAPES)
-@pytest.mark.parametrize("path", [AUTO, SKINNY, WIDE])
+@pytest.mark.parametrize("path", [AUTO, SKINNY, WIDE, PHASED])
 def test_mlp_random(shape, path):
     M, d, dff, dtype = shape
-    if path == WIDE and dtype == F32:
+    if path in (WIDE, PHASED) and dtype == F32:
         pytest.skip("the wide path is bf16 only")
     say("mlp", shape, "path", path)
     inp = wl.random_inputs(M + 3 * d, M, d, dff, dtype, with_down=True)
@@ -121,12 +122,13 @@ def test_mlp_random(shape, path):
 
 
 # ---------------------------------------------------------------- exact closed forms
-@pytest.mark.parametrize("dtype,path", [(BF16, SKINNY), (BF16, WIDE), (F32, SKINNY)])
+@pytest.mark.parametrize("dtype,path", [(BF16, SKINNY), (BF16, WIDE), (BF16, PHASED),
+                                        (F32, SKINNY)])
 def test_integer_inputs_exact_products(dtype, path):
     # |x|, |w| <= 4 and d <= 1000: every product and partial sum is an integer
     # below 2^24, exact in fp32 in any order, so only silu and the final
     # rounding separate the GPU from the oracle.
-    M, d, dff = (80, 1000, 520) if path == WIDE else (12, 1000, 520)
+    M, d, dff = (12, 1000, 520) if path == SKINNY else (80, 1000, 520)
     say("integer exact", dtype, path)
     inp = wl.integer_inputs(5, M, d, dff, dtype)
     wp, _ = pack(inp, d, dff, dtype)
@@ -137,7 +139,7 @@ def test_integer_inputs_exact_products(dtype, path):
     assert np.all(np.abs(out - ref) <= bound), compare(out, ref, rel)
 
 
-@pytest.mark.parametrize("path", [SKINNY, WIDE])
+@pytest.mark.parametrize("path", [SKINNY, WIDE, PHASED])
 def test_zero_input_gives_exact_zero(path):
     M, d, dff = 70, 256, 384
     inp = wl.random_inputs(9, M, d, dff, BF16, with_down=True)
@@ -147,7 +149,7 @@ def test_zero_input_gives_exact_zero(path):
     assert not host(run_mlp(x0, wp, wdp, M, d, dff, BF16, path), BF16).any()
 
 
-@pytest.mark.parametrize("path", [SKINNY, WIDE])
+@pytest.mark.parametrize("path", [SKINNY, WIDE, PHASED])
 def test_one_hot_rows_select_weight_rows(path):
     M, d, dff = 72, 320, 264
     ks = [(37 * m) % d for m in range(M)]
@@ -161,7 +163,7 @@ def test_one_hot_rows_select_weight_rows(path):
 
 
 # ---------------------------------------------------------------- metamorphic (bitwise)
-@pytest.mark.parametrize("path", [SKINNY, WIDE])
+@pytest.mark.parametrize("path", [SKINNY, WIDE, PHASED])
 def test_determinism_bitwise(path):
     M, d, dff = (16, 2048, 3072) if path == SKINNY else (300, 1024, 1536)
     inp = wl.random_inputs(17, M, d, dff, BF16)
@@ -172,7 +174,7 @@ def test_determinism_bitwise(path):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("path", [SKINNY, WIDE])
+@pytest.mark.parametrize("path", [SKINNY, WIDE, PHASED])
 def test_linearity_in_up_weight_bitwise(path):
     # out(x, Wg, 2 Wu) = 2 out(x, Wg, Wu): power-of-two scaling is exact
     M, d, dff = (8, 512, 640) if path == SKINNY else (128, 512, 640)
@@ -187,7 +189,7 @@ def test_linearity_in_up_weight_bitwise(path):
     assert np.array_equal(o2, 2.0 * o1)
 
 
-@pytest.mark.parametrize("path", [SKINNY, WIDE])
+@pytest.mark.parametrize("path", [SKINNY, WIDE, PHASED])
 def test_joint_column_permutation_bitwise(path):
     M, d, dff = (4, 256, 512) if path == SKINNY else (96, 256, 512)
     inp = wl.random_inputs(23, M, d, dff, BF16)
@@ -238,6 +240,21 @@ def test_paths_agree_where_both_apply():
     assert_close(b, ref, BF16)
     # two correct fp32-accumulated orders differ by at most a couple of bf16 ulps
     assert np.all(np.abs(a - b) <= 2 * 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-3)
+
+
+@pytest.mark.parametrize("shape", [(96, 768, 1024), (300, 1000, 1400), (257, 520, 2056),
+                                   (1024, 4096, 1536)])
+def test_two_pass_schedule_is_bitwise_the_one_pass_result(shape):
+    # Both schedules sum every accumulator over the same MFMAs in the same
+    # K order and apply silu(gate) * up in fp32, so they agree bit for bit.
+    M, d, dff = shape
+    say("phased vs wide", shape)
+    inp = wl.random_inputs(43 + M, M, d, dff, BF16)
+    wp, _ = pack(inp, d, dff, BF16)
+    x = dev(inp["x"])
+    a = run_up(x, wp, M, d, dff, BF16, WIDE).cpu().numpy()
+    b = run_up(x, wp, M, d, dff, BF16, PHASED).cpu().numpy()
+    assert np.array_equal(a, b)
 
 
 def test_empty_batch_is_a_noop():
