@@ -70,7 +70,7 @@ def traffic_from_profile(workload: str, kernel: str):
 class Runner:
     """Device buffers and the C-ABI call for one workload."""
 
-    def __init__(self, w: wl.Workload, copies: int, path: int = 0):
+    def __init__(self, w: wl.Workload, copies: int, path: int = 0, graph: bool = False):
         import torch
         import gemv_gate_up_amd as sw
         self.torch, self.sw, self.w = torch, sw, w
@@ -113,11 +113,30 @@ class Runner:
         self.args = [(self.x.data_ptr(), self.wps[i].data_ptr(),
                       self.wdps[i].data_ptr() if self.wdps[i] is not None else None)
                      for i in range(copies)]
+        # with graph=True, one recorded call per weight copy; a step replays one
+        self.graphs = []
+        for i in range(copies if graph else 0):
+            xp, wpp, wdpp = self.args[i]
+            if w.with_down:
+                rc, g = sw.mlp_forward_graph_create(xp, wpp, wdpp, self.out, w.M, w.d, w.dff,
+                                                    w.dtype, self.ws, self.ws_bytes, path)
+            else:
+                rc, g = sw.swiglu_up_graph_create(xp, wpp, self.out, w.M, w.d, w.dff, w.dtype,
+                                                  self.ws, self.ws_bytes, path)
+            sw.check(rc, "graph create")
+            self.graphs.append(g)
+
+    def close(self) -> None:
+        for g in self.graphs:
+            self.sw.swiglu_graph_destroy(g)
+        self.graphs = []
 
     def step(self, i: int) -> None:
         w, sw = self.w, self.sw
         xp, wpp, wdpp = self.args[i % self.copies]
-        if self.req_path and w.with_down:
+        if self.graphs:
+            rc = sw._lib.swiglu_graph_launch(self.graphs[i % self.copies], self.sh)
+        elif self.req_path and w.with_down:
             rc = sw._lib.mlp_forward_ex(xp, wpp, wdpp, self.out.data_ptr(), w.M, w.d, w.dff,
                                         w.dtype, self.ws.data_ptr(), self.ws_bytes, self.sh,
                                         self.req_path)
@@ -164,8 +183,9 @@ def dominant_kernel(w: wl.Workload, path: int) -> str:
     return "skinny_bf16_kernel" if w.dtype == wl.BF16 else "skinny_f32_kernel"
 
 
-def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0) -> dict:
-    r = Runner(w, copies, path)
+def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0,
+            graph: bool = False) -> dict:
+    r = Runner(w, copies, path, graph)
     t = r.time(steps, warmup)
     kern = dominant_kernel(w, r.path)
     per_launch_ms = t["event_ms_per_launch"]
@@ -250,6 +270,8 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay recorded calls (HIP graphs) instead of direct calls")
     ap.add_argument("--path", default="auto", choices=sorted(PATHS),
                     help="force a kernel path for the main workload (default: the dispatcher's)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -272,7 +294,7 @@ def main() -> int:
     one_copy = 2 * w.d * w.dff * w.elem_bytes
     copies = max(1, -(-(1 << 30) // one_copy)) if one_copy < (1 << 30) else 1
     log("workload %s: %s, %d weight copies" % (w.name, w, copies))
-    m = measure(w, args.steps, args.warmup, copies, PATHS[args.path])
+    m = measure(w, args.steps, args.warmup, copies, PATHS[args.path], args.graph)
     t = m["timing"]
     value_bytes = w.algorithmic_bytes() / (t["wall_ms_per_step"] * 1e-3) / 1e9
     rec = {
@@ -290,13 +312,15 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights, bf16 RNE)",
         "config": {"workload": w.name, "M": w.M, "d": w.d, "dff": w.dff,
                    "with_down": w.with_down, "path": PATH_NAMES[m["path"]],
-                   "weight_copies": copies, "algorithmic_bytes": w.algorithmic_bytes(),
+                   "weight_copies": copies, "graph": bool(args.graph),
+                   "algorithmic_bytes": w.algorithmic_bytes(),
                    "algorithmic_flops": w.algorithmic_flops()},
         "roofline": m["roofline"],
         "timing_ms": {k: round(v, 5) for k, v in t.items()},
     }
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, m["runner"].inp, args.cpu_seconds)
+    m["runner"].close()
     del m
     torch.cuda.empty_cache()
     if not args.no_prefill and w.name != "prefill8b_m4096":

@@ -42,6 +42,18 @@ class SwigluError(RuntimeError):
         super().__init__("%s: %s (%d)" % (what or "swiglu", swiglu_status_string(status), status))
 
 
+# One HIP runtime per process.  PyTorch's ROCm wheel ships its own
+# libamdhip64 and links it under a name (libamdhip64.so) that differs from
+# the one this library links (libamdhip64.so.7, found under /opt/rocm).  If
+# this library were loaded first, importing torch afterwards would map a
+# second runtime, and device pointers and streams from one runtime are not
+# valid in the other.  Importing torch first makes the dynamic linker bind
+# this library to the runtime already in the process (same soname).
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:   # a process without torch has only one runtime anyway
+    _torch = None
+
 if not os.path.exists(LIB_PATH):
     raise ImportError("libswiglu.so is not built; run `python gemv_gate_up_amd/build.py` "
                       "(expected at %s)" % LIB_PATH)
@@ -63,6 +75,12 @@ _SIGS = {
     "swiglu_up_ex": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _vp, _int]),
     "mlp_forward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
     "mlp_forward_ex": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _vp, _int]),
+    "swiglu_up_graph_create": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _int,
+                                      ctypes.POINTER(_vp)]),
+    "mlp_forward_graph_create": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz,
+                                        _int, ctypes.POINTER(_vp)]),
+    "swiglu_graph_launch": (_int, [_vp, _vp]),
+    "swiglu_graph_destroy": (_int, [_vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -153,6 +171,33 @@ def mlp_forward_ex(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace=None, wo
                    stream=None, path=SWIGLU_PATH_AUTO) -> int:
     return _lib.mlp_forward_ex(_ptr(x), _ptr(Wpacked), _ptr(Wdpacked), _ptr(y), M, d, dff,
                                dtype, _ptr(workspace), workspace_bytes, _stream(stream), path)
+
+
+def swiglu_up_graph_create(x, Wpacked, out, M, d, dff, dtype, workspace=None, workspace_bytes=0,
+                           path=SWIGLU_PATH_AUTO):
+    """Returns (status, handle); the handle (an int) is None unless status is 0."""
+    h = _vp()
+    rc = _lib.swiglu_up_graph_create(_ptr(x), _ptr(Wpacked), _ptr(out), M, d, dff, dtype,
+                                     _ptr(workspace), workspace_bytes, path, ctypes.byref(h))
+    return rc, h.value
+
+
+def mlp_forward_graph_create(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace=None,
+                             workspace_bytes=0, path=SWIGLU_PATH_AUTO):
+    """Returns (status, handle); the handle (an int) is None unless status is 0."""
+    h = _vp()
+    rc = _lib.mlp_forward_graph_create(_ptr(x), _ptr(Wpacked), _ptr(Wdpacked), _ptr(y), M, d,
+                                       dff, dtype, _ptr(workspace), workspace_bytes, path,
+                                       ctypes.byref(h))
+    return rc, h.value
+
+
+def swiglu_graph_launch(graph, stream=None) -> int:
+    return _lib.swiglu_graph_launch(graph, _stream(stream))
+
+
+def swiglu_graph_destroy(graph) -> int:
+    return _lib.swiglu_graph_destroy(graph)
 
 
 def check(status: int, what: str = "") -> None:

@@ -10,8 +10,15 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <new>
+
 #include "launch.h"
 #include "swiglu.h"
+
+struct swiglu_graph_s {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
 
 namespace swg {
 namespace {
@@ -138,8 +145,10 @@ int run(const GemmArgs& g, int path, void* partial, hipStream_t s)
     return e == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_HIP;
 }
 
+// do_up / do_mlp check every argument, then launch unless `launch` is
+// false (the graph-creation calls validate before touching HIP).
 int do_up(const void* x, const void* wp, void* out, int64_t M, int64_t d, int64_t dff, int dtype,
-          void* ws, size_t ws_bytes, hipStream_t s, int path)
+          void* ws, size_t ws_bytes, hipStream_t s, int path, bool launch = true)
 {
     int rc = check_sizes(M, d, dff, dtype);
     if (rc == SWIGLU_OK)
@@ -159,6 +168,8 @@ int do_up(const void* x, const void* wp, void* out, int64_t M, int64_t d, int64_
         return (int)need;
     if ((size_t)need > ws_bytes || (need > 0 && !ws))
         return SWIGLU_ERR_WORKSPACE;
+    if (!launch)
+        return SWIGLU_OK;
     g.a = x;
     g.w = wp;
     g.out = out;
@@ -166,7 +177,8 @@ int do_up(const void* x, const void* wp, void* out, int64_t M, int64_t d, int64_
 }
 
 int do_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, int64_t d,
-           int64_t dff, int dtype, void* ws, size_t ws_bytes, hipStream_t s, int path)
+           int64_t dff, int dtype, void* ws, size_t ws_bytes, hipStream_t s, int path,
+           bool launch = true)
 {
     int rc = check_sizes(M, d, dff, dtype);
     if (rc == SWIGLU_OK)
@@ -189,6 +201,8 @@ int do_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, i
         return (int)need;
     if ((size_t)need > ws_bytes)
         return SWIGLU_ERR_WORKSPACE;
+    if (!launch)
+        return SWIGLU_OK;
     uint8_t* h = (uint8_t*)ws;
     uint8_t* partial = h + h_bytes(M, d, dff, dtype);
     u.a = x;
@@ -201,6 +215,53 @@ int do_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, i
     dn.w = wdp;
     dn.out = y;
     return run(dn, pd, partial, s);
+}
+
+// Records one call (`call(stream, launch)` returns a status) on a private
+// stream and instantiates it.  The arguments are checked first, without any
+// HIP call; the launch attributes are set before the capture so that the
+// recording holds kernel launches only.
+template <class Call>
+int record_graph(Call&& call, swiglu_graph_t* out)
+{
+    if (!out)
+        return SWIGLU_ERR_INVALID_ARG;
+    *out = nullptr;
+    int rc = call(nullptr, false);
+    if (rc != SWIGLU_OK)
+        return rc;
+    if (wide_prepare() != hipSuccess)
+        return SWIGLU_ERR_HIP;
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess)
+        return SWIGLU_ERR_HIP;
+    rc = SWIGLU_ERR_HIP;
+    hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) == hipSuccess) {
+        rc = call(s, true);
+        // the capture is always ended, also when the call was rejected
+        if (hipStreamEndCapture(s, &graph) != hipSuccess && rc == SWIGLU_OK)
+            rc = SWIGLU_ERR_HIP;
+    }
+    hipGraphExec_t exec = nullptr;
+    if (rc == SWIGLU_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
+        rc = SWIGLU_ERR_HIP;
+    hipStreamDestroy(s);
+    swiglu_graph_s* h = nullptr;
+    if (rc == SWIGLU_OK) {
+        h = new (std::nothrow) swiglu_graph_s{graph, exec};
+        if (!h) {
+            hipGraphExecDestroy(exec);
+            rc = SWIGLU_ERR_HIP;
+        }
+    }
+    if (rc != SWIGLU_OK) {
+        if (graph)
+            hipGraphDestroy(graph);
+        return rc;
+    }
+    *out = h;
+    return SWIGLU_OK;
 }
 
 int do_pack(const void* src0, const void* src1, void* dst, const PackGeom& g, int plain,
@@ -321,6 +382,47 @@ int mlp_forward_ex(const void* x, const void* Wpacked, const void* Wdpacked, voi
 {
     return do_mlp(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace, workspace_bytes, stream,
                   path);
+}
+
+int swiglu_up_graph_create(const void* x, const void* Wpacked, void* out, int64_t M, int64_t d,
+                           int64_t dff, int dtype, void* workspace, size_t workspace_bytes,
+                           int path, swiglu_graph_t* graph)
+{
+    return record_graph(
+        [&](hipStream_t s, bool launch) {
+            return do_up(x, Wpacked, out, M, d, dff, dtype, workspace, workspace_bytes, s, path,
+                         launch);
+        },
+        graph);
+}
+
+int mlp_forward_graph_create(const void* x, const void* Wpacked, const void* Wdpacked, void* y,
+                             int64_t M, int64_t d, int64_t dff, int dtype, void* workspace,
+                             size_t workspace_bytes, int path, swiglu_graph_t* graph)
+{
+    return record_graph(
+        [&](hipStream_t s, bool launch) {
+            return do_mlp(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace, workspace_bytes, s,
+                          path, launch);
+        },
+        graph);
+}
+
+int swiglu_graph_launch(swiglu_graph_t graph, hipStream_t stream)
+{
+    if (!graph)
+        return SWIGLU_ERR_INVALID_ARG;
+    return hipGraphLaunch(graph->exec, stream) == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_HIP;
+}
+
+int swiglu_graph_destroy(swiglu_graph_t graph)
+{
+    if (!graph)
+        return SWIGLU_OK;
+    hipGraphExecDestroy(graph->exec);
+    hipGraphDestroy(graph->graph);
+    delete graph;
+    return SWIGLU_OK;
 }
 
 }  // extern "C"

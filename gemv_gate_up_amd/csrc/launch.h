@@ -47,5 +47,8 @@ hipError_t launch_wide(const GemmArgs& g, hipStream_t s);
 // Two-pass (gate K loop, then up K loop) schedule; gate/up products only.
 hipError_t launch_wide_phased(const GemmArgs& g, hipStream_t s);
 int wide_supported(const GemmArgs& g);
+// Sets the launch attributes of every wide instantiation (host calls only);
+// done before a stream capture so that none of them is recorded inside it.
+hipError_t wide_prepare();
 
 }  // namespace swg

@@ -28,6 +28,18 @@ int wide_supported(const GemmArgs& g)
            (int64_t)(WideCfg::BN / 32) * g.geom.nkc * 2 * PIECE_BYTES < ((int64_t)1 << 32);
 }
 
+hipError_t wide_prepare()
+{
+    using C = WideCfg;
+    using P = WidePhasedCfg;
+    hipError_t e = wide_attrs<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_SWIGLU>();
+    if (e == hipSuccess)
+        e = wide_attrs<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_PLAIN>();
+    if (e == hipSuccess)
+        e = wide_attrs<P::BM, P::BN, P::WGM, P::WGN, P::KCS, P::STAGES, EPI_SWIGLU, true>();
+    return e;
+}
+
 hipError_t launch_wide(const GemmArgs& g, hipStream_t s)
 {
     using C = WideCfg;

@@ -390,20 +390,35 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     }
 }
 
+// Raises one instantiation's dynamic LDS limit to its ring size, once per
+// process (a function-local static: thread-safe, and the host call is made
+// outside any later stream capture when the library's prepare step runs
+// first).
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED>
+static hipError_t wide_attr()
+{
+    using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
+    static const hipError_t e = hipFuncSetAttribute(
+        (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
+    return e;
+}
+
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED = false>
+hipError_t wide_attrs()
+{
+    hipError_t e = wide_attr<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED>();
+    return e != hipSuccess ? e : wide_attr<BM, BN, WGM, WGN, KCS, STAGES, EPI, true, PHASED>();
+}
+
 // Host launcher for one configuration.
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED>
 static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m)
 {
     using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
-    static bool attr_set = false;   // benign race: every writer stores the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED>,
-            hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    const hipError_t e = wide_attr<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED>();
+    if (e != hipSuccess)
+        return e;
     const int tiles_m = (int)ceil_div(g.M, BM);
     const int tiles_n = (int)ceil_div(ceil_div(g.ncols_out, g.geom.cols_per_pb), S::PB_TILE);
     wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED>

@@ -15,11 +15,14 @@
  *   - Pointers named x, w*, out, y and workspace are DEVICE pointers on the
  *     current HIP device; the caller allocates and owns them.  The library
  *     keeps no pointer after a call returns and holds no mutable global
- *     state, so calls are thread-safe.
+ *     state, so calls are thread-safe (the graph handles at the end of
+ *     this header are the one exception: they keep the pointers they were
+ *     captured with).
  *   - dtype is SWIGLU_BF16 (bf16 storage, fp32 accumulation, bf16 output)
  *     or SWIGLU_F32 (fp32 storage and arithmetic).  x, the weights and the
  *     output share one dtype.
- *   - Calls only enqueue kernels on `stream`: no allocation, no copy, no
+ *   - Calls only enqueue kernels on `stream` (the graph-creation calls
+ *     excepted): no allocation, no copy, no
  *     synchronisation (the decode-path conventions of "Où part le temps d'un
  *     token": fixed buffers, no per-call allocation, no host waits).  A
  *     return of SWIGLU_OK means the arguments were valid and the launches
@@ -155,6 +158,48 @@ int mlp_forward(const void *x, const void *Wpacked, const void *Wdpacked, void *
 int mlp_forward_ex(const void *x, const void *Wpacked, const void *Wdpacked, void *y,
                    int64_t M, int64_t d, int64_t dff, int dtype,
                    void *workspace, size_t workspace_bytes, hipStream_t stream, int path);
+
+/*
+ * Recorded calls (HIP graphs).  A per-kernel fixed cost (launch, ramp-up,
+ * drain) dominates short calls; replaying a recorded sequence of launches
+ * from one host call is one of the two remedies that "Où part le temps d'un
+ * token" names in its section on what remains (the launches), fusion being
+ * the other.  As that section notes, a recording replays the same kernels
+ * on the same buffers with the same sizes: every pointer and size given to
+ * a *_graph_create call is fixed in the graph.  To reuse it, overwrite x
+ * (and the weights, if they change) in place and launch again; out/y are
+ * rewritten by each launch.
+ *
+ * swiglu_up_graph_create / mlp_forward_graph_create validate their
+ * arguments exactly as swiglu_up_ex / mlp_forward_ex do (same status
+ * codes; nothing is created on error), then record that one call on a
+ * private stream of the current device and instantiate it.  They allocate
+ * host and HIP objects, so they belong to set-up, not to the per-call path.
+ * On success *graph receives a handle owned by the caller; the buffers must
+ * outlive it.  M == 0 records an empty graph.
+ *
+ * swiglu_graph_launch enqueues one replay on `stream` (any stream of the
+ * device the graph was created on); replays on one stream run in order,
+ * and replays that share a workspace must not run concurrently.  Returns
+ * SWIGLU_ERR_INVALID_ARG for a NULL handle, SWIGLU_ERR_HIP if the launch is
+ * refused.  swiglu_graph_destroy releases the handle (NULL is a no-op); it
+ * must not be called while a replay may still be running.
+ */
+typedef struct swiglu_graph_s *swiglu_graph_t;
+
+int swiglu_up_graph_create(const void *x, const void *Wpacked, void *out,
+                           int64_t M, int64_t d, int64_t dff, int dtype,
+                           void *workspace, size_t workspace_bytes, int path,
+                           swiglu_graph_t *graph);
+
+int mlp_forward_graph_create(const void *x, const void *Wpacked, const void *Wdpacked, void *y,
+                             int64_t M, int64_t d, int64_t dff, int dtype,
+                             void *workspace, size_t workspace_bytes, int path,
+                             swiglu_graph_t *graph);
+
+int swiglu_graph_launch(swiglu_graph_t graph, hipStream_t stream);
+
+int swiglu_graph_destroy(swiglu_graph_t graph);
 
 #ifdef __cplusplus
 }

@@ -116,3 +116,30 @@ def test_workloads_shapes_are_supported():
     for w in wl.WORKLOADS.values():
         assert sw.swiglu_packed_bytes(w.d, w.dff, w.dtype) > 0
         assert sw.swiglu_select_path(w.M, w.d, w.dff, w.dtype) in (1, 2)
+
+
+def test_graph_create_rejects_bad_arguments_before_any_hip_call():
+    # the same checks as the direct calls, made before a stream is created
+    rc, h = sw.swiglu_up_graph_create(FAKE, FAKE, FAKE, -1, 64, 64, BF16)
+    assert (rc, h) == (sw.SWIGLU_ERR_INVALID_ARG, None)
+    rc, h = sw.swiglu_up_graph_create(FAKE + 4, FAKE, FAKE, 4, 64, 64, BF16)
+    assert (rc, h) == (sw.SWIGLU_ERR_MISALIGNED, None)
+    rc, h = sw.swiglu_up_graph_create(FAKE, FAKE, FAKE, 1, 512, 2048, F32, None, 0)
+    assert (rc, h) == (sw.SWIGLU_ERR_WORKSPACE, None)
+    rc, h = sw.swiglu_up_graph_create(FAKE, FAKE, FAKE, 4, 64, 64, F32, None, 0,
+                                      sw.SWIGLU_PATH_WIDE)
+    assert (rc, h) == (sw.SWIGLU_ERR_UNSUPPORTED, None)
+    rc, h = sw.mlp_forward_graph_create(FAKE, FAKE, FAKE, FAKE, 4, 64, 64, BF16, None, 0)
+    assert (rc, h) == (sw.SWIGLU_ERR_INVALID_ARG, None)
+    assert sw._lib.swiglu_up_graph_create(FAKE, FAKE, FAKE, 4, 64, 64, BF16, None, 0, 0,
+                                          None) == sw.SWIGLU_ERR_INVALID_ARG
+    assert sw.swiglu_graph_launch(None, 0) == sw.SWIGLU_ERR_INVALID_ARG
+    assert sw.swiglu_graph_destroy(None) == sw.SWIGLU_OK
+
+
+def test_one_hip_runtime_in_the_process():
+    # importing the binding must not map a second libamdhip64 beside torch's
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read().split("\n")
+    files = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(files) == 1, files
