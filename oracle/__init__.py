@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
+F64 = 2
 
 _lib = None
 
@@ -60,6 +61,16 @@ def _bind(lib):
                                     vp, i64, dp, dp, ctypes.c_int]
     lib.oracle_default_threads.restype = ctypes.c_int
     lib.oracle_default_threads.argtypes = []
+    lib.oracle_bf16_array_to_double.restype = ctypes.c_int
+    lib.oracle_bf16_array_to_double.argtypes = [vp, i64, dp]
+    lib.oracle_e4m3_to_double.restype = ctypes.c_double
+    lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_from_float.restype = ctypes.c_uint8
+    lib.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
+    lib.oracle_quantize_e4m3_columns.restype = ctypes.c_int
+    lib.oracle_quantize_e4m3_columns.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_dequantize_e4m3_columns.restype = ctypes.c_int
+    lib.oracle_dequantize_e4m3_columns.argtypes = [vp, vp, i64, i64, dp]
     return lib
 
 
@@ -79,7 +90,9 @@ def _dtype_of(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError("oracle inputs are float32 arrays or uint16 bf16 bit patterns")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError("oracle inputs are float32 or float64 arrays, or uint16 bf16 bit patterns")
 
 
 def _check(x, wg, wu, wd=None):
@@ -141,6 +154,64 @@ def mlp(x, wg, wu, wd, rows=None, want_h=False, nthreads=0, lib=None):
     if rc != 0:
         raise ValueError("oracle_mlp_rows failed (%d)" % rc)
     return (y, h) if want_h else y
+
+
+def bf16_array_to_double(a, lib=None) -> np.ndarray:
+    """Exact widening of a uint16 array of bf16 patterns."""
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    out = np.empty(a.shape, dtype=np.float64)
+    if (lib or _load()).oracle_bf16_array_to_double(_ptr(a), a.size, _ptr(out)) != 0:
+        raise ValueError("oracle_bf16_array_to_double failed")
+    return out
+
+
+def e4m3_to_double(code: int, lib=None) -> float:
+    return (lib or _load()).oracle_e4m3_to_double(int(code))
+
+
+def e4m3_from_float(v: float, lib=None) -> int:
+    """Nearest E4M3 code (ties to even, saturating) of the fp32 value v."""
+    return (lib or _load()).oracle_e4m3_from_float(float(np.float32(v)))
+
+
+def quantize_e4m3(w, lib=None):
+    """Per-column E4M3 quantisation of a K x N bf16 matrix (uint16 bits):
+    returns (codes uint8 K x N, scales float32 N)."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    K, N = w.shape
+    codes = np.empty((K, N), dtype=np.uint8)
+    scales = np.empty(N, dtype=np.float32)
+    if (lib or _load()).oracle_quantize_e4m3_columns(_ptr(w), K, N, _ptr(codes), _ptr(scales)):
+        raise ValueError("oracle_quantize_e4m3_columns failed")
+    return codes, scales
+
+
+def dequantize_e4m3(codes, scales, lib=None) -> np.ndarray:
+    """scale[n] * e4m3(code[k][n]) in fp64."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    K, N = codes.shape
+    if scales.shape != (N,):
+        raise ValueError("one scale per column")
+    out = np.empty((K, N), dtype=np.float64)
+    if (lib or _load()).oracle_dequantize_e4m3_columns(_ptr(codes), _ptr(scales), K, N,
+                                                       _ptr(out)):
+        raise ValueError("oracle_dequantize_e4m3_columns failed")
+    return out
+
+
+def swiglu_fp8w(x, qg, sg, qu, su, rows=None, nthreads=0, lib=None):
+    """silu(x.Wg) * (x.Wu) with Wg, Wu given as E4M3 codes and column scales
+    (x in bf16 bits): the fp64 product of x and the dequantised weights."""
+    return swiglu(bf16_array_to_double(x, lib), dequantize_e4m3(qg, sg, lib),
+                  dequantize_e4m3(qu, su, lib), rows=rows, nthreads=nthreads, lib=lib)
+
+
+def mlp_fp8w(x, qg, sg, qu, su, qd, sd, rows=None, nthreads=0, lib=None):
+    """The full MLP with all three weights given as E4M3 codes and scales."""
+    return mlp(bf16_array_to_double(x, lib), dequantize_e4m3(qg, sg, lib),
+               dequantize_e4m3(qu, su, lib), dequantize_e4m3(qd, sd, lib), rows=rows,
+               nthreads=nthreads, lib=lib)
 
 
 def default_threads() -> int:

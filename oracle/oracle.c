@@ -17,7 +17,8 @@
  *
  * Inputs are the exact bits handed to the GPU: fp32 arrays, or bf16 stored
  * as raw uint16 patterns, which are widened exactly (bits << 16 -> float ->
- * double).  Every element of g, u and y is a sum taken in ascending order of
+ * double); or fp64 arrays (the dequantised FP8 weights below, with x
+ * widened from bf16).  Every element of g, u and y is a sum taken in ascending order of
  * the contraction index.  Threads only split independent output elements,
  * so results do not depend on the thread count.  h is never rounded before
  * the down projection.
@@ -25,6 +26,18 @@
  * Layouts: x is M x d, Wgate and Wup are d x dff, Wdown is dff x d, all
  * row-major.  Parity pins: tests/test_oracle.py (closed forms, integer-exact
  * products, one-hot rows, brute force on tiny shapes).
+ *
+ * FP8 weights.  "Tile-Level Activation Overlap for Efficient LLM
+ * Inference" (section on the problem) notes that quantised weights make the
+ * memory-bound part of the MLP weigh more; the pages fix no scheme.  The
+ * one used here: OCP 8-bit E4M3 codes (the variant with no infinities), one
+ * fp32 scale per output column equal to the column's largest magnitude over
+ * 448 (the largest E4M3 value), codes rounded to nearest with ties to the
+ * even code and saturated at +-448.  The scale and w / scale are fp32
+ * divisions, as on the GPU, so both sides take the same rounding decisions;
+ * everything after that is exact in fp64.  Pins: tests/test_oracle.py
+ * (format constants, brute-force nearest search, exact grids, error
+ * bounds).
  */
 #include <math.h>
 #include <stdint.h>
@@ -36,6 +49,7 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2
 
 /* bf16 is the top 16 bits of an IEEE binary32; widening is exact. */
 double oracle_bf16_to_double(uint16_t bits)
@@ -50,7 +64,103 @@ static inline double elem(const void *p, int dtype, int64_t i)
 {
     if (dtype == ORACLE_F32)
         return (double)((const float *)p)[i];
+    if (dtype == ORACLE_F64)
+        return ((const double *)p)[i];
     return oracle_bf16_to_double(((const uint16_t *)p)[i]);
+}
+
+/* Exact widening of n bf16 patterns. */
+int oracle_bf16_array_to_double(const uint16_t *src, int64_t n, double *dst)
+{
+    if (n < 0 || (n > 0 && (!src || !dst)))
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = oracle_bf16_to_double(src[i]);
+    return 0;
+}
+
+/*
+ * E4M3 value of a code: sign bit, 4-bit exponent field e with bias 7, 3-bit
+ * mantissa m.  e = 0 holds the subnormals m * 2^-9; otherwise the value is
+ * (1 + m/8) * 2^(e-7).  Exponent 15 with mantissa 7 is NaN; there is no
+ * infinity, so 0x7E = 1.75 * 2^8 = 448 is the largest finite value.
+ */
+double oracle_e4m3_to_double(uint8_t code)
+{
+    int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return s ? -v : v;
+}
+
+/*
+ * Nearest E4M3 code to v; ties go to the even code; magnitudes of 448 and
+ * above saturate to +-448.  Works on |v| in fp64 (exact for any fp32 v):
+ * within a binade [2^b, 2^(b+1)) the E4M3 values are spaced 2^(b-3), and
+ * below 2^-6 they are spaced 2^-9, so rounding |v| / spacing to the nearest
+ * even integer (the default rounding mode) picks the code; the integer is
+ * 8 + mantissa in a binade and the mantissa itself below 2^-6, so an even
+ * integer is an even code.
+ */
+uint8_t oracle_e4m3_from_float(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int e;
+    frexp(a, &e);                   /* a = f * 2^e with f in [0.5, 1) */
+    int b = e - 1;                  /* binade of a: 2^b <= a < 2^(b+1) */
+    double spacing = (a == 0.0 || b < -6) ? ldexp(1.0, -9) : ldexp(1.0, b - 3);
+    double r = nearbyint(a / spacing) * spacing;
+    if (r < ldexp(1.0, -6))
+        return sign | (uint8_t)(r / ldexp(1.0, -9));
+    frexp(r, &e);
+    b = e - 1;
+    int m = (int)(r / ldexp(1.0, b - 3)) - 8;
+    return sign | (uint8_t)(((b + 7) << 3) | m);
+}
+
+/*
+ * Quantises the K x N row-major bf16 matrix w column by column: scale[n] =
+ * max_k |w[k][n]| / 448 and code[k][n] = e4m3(w[k][n] / scale[n]), both
+ * divisions in fp32; a column of zeros gets scale 0 and code 0 throughout.
+ */
+int oracle_quantize_e4m3_columns(const uint16_t *w, int64_t K, int64_t N, uint8_t *codes,
+                                 float *scales)
+{
+    if (K <= 0 || N <= 0 || !w || !codes || !scales)
+        return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf((float)oracle_bf16_to_double(w[k * N + n]));
+            if (a > amax)
+                amax = a;
+        }
+        float s = amax / 448.0f;
+        scales[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            float x = (float)oracle_bf16_to_double(w[k * N + n]);
+            codes[k * N + n] = s == 0.0f ? 0 : oracle_e4m3_from_float(x / s);
+        }
+    }
+    return 0;
+}
+
+/* out[k][n] = scale[n] * e4m3(code[k][n]), exact in fp64. */
+int oracle_dequantize_e4m3_columns(const uint8_t *codes, const float *scales, int64_t K,
+                                   int64_t N, double *out)
+{
+    if (K <= 0 || N <= 0 || !codes || !scales || !out)
+        return -1;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            out[k * N + n] = (double)scales[n] * oracle_e4m3_to_double(codes[k * N + n]);
+    return 0;
 }
 
 /* Logistic function 1/(1+e^-z), written so that exp never overflows. */
@@ -70,7 +180,8 @@ double oracle_silu(double z)
 
 static int bad_dims(int dtype, int64_t M, int64_t d, int64_t dff)
 {
-    return (dtype != ORACLE_F32 && dtype != ORACLE_BF16) || M < 0 || d <= 0 || dff <= 0;
+    return (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) || M < 0 ||
+           d <= 0 || dff <= 0;
 }
 
 static int threads_or_default(int nthreads)

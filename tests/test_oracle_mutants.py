@@ -30,6 +30,19 @@ MUTANTS = {
                      "us[n - n0] += xv * elem(wg, dtype, k * dff + n);"),
     "dropped_last_down_term": ("for (int64_t n = 0; n < dff; ++n) {\n                    double hv",
                                "for (int64_t n = 0; n < dff - 1; ++n) {\n                    double hv"),
+    # FP8 weight format and quantiser
+    "e4m3_bias": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)"),
+    "e4m3_subnormal_step": ("double v = e == 0 ? ldexp((double)m, -9)",
+                            "double v = e == 0 ? ldexp((double)m, -10)"),
+    "e4m3_ties_away": ("nearbyint(a / spacing)", "round(a / spacing)"),
+    "e4m3_no_saturation": ("if (a >= 448.0)\n        return sign | 0x7E;",
+                           "if (a >= 480.0)\n        return sign | 0x7E;"),
+    "scale_wrong_max": ("float s = amax / 448.0f;", "float s = amax / 240.0f;"),
+    "quantize_unscaled": ("oracle_e4m3_from_float(x / s)", "oracle_e4m3_from_float(x)"),
+    "dequantize_unscaled": ("out[k * N + n] = (double)scales[n] * oracle_e4m3_to_double",
+                            "out[k * N + n] = oracle_e4m3_to_double"),
+    "f64_read_as_f32": ("return ((const double *)p)[i];",
+                        "return (double)((const float *)p)[i];"),
 }
 
 
@@ -49,6 +62,32 @@ def pin_failures(lib):
             failed.append(name)
 
     check("bf16", lambda: oracle.bf16_to_double(0x4049, lib=lib) == 3.140625)
+    # E4M3 values and codes fixed by the format (worked by hand: 0.3 lies in
+    # [2^-2, 2^-1), spacing 2^-5, 9.6 steps -> 10 -> 1.25 * 2^-2 = code 0x2A)
+    check("e4m3_decode", lambda: [oracle.e4m3_to_double(c, lib=lib) for c in (0x01, 0x08, 0x38, 0x7E)]
+          == [2.0 ** -9, 2.0 ** -6, 1.0, 448.0])
+    enc = [(1.0625, 0x38), (1.1875, 0x3A), (3 * 2.0 ** -10, 0x02), (7.5 * 2.0 ** -9, 0x08),
+           (475.0, 0x7E), (-1e9, 0xFE), (5.5, 0x4B), (0.3, 0x2A)]
+    check("e4m3_encode", lambda: all(oracle.e4m3_from_float(v, lib=lib) == c for v, c in enc))
+
+    def quant_grid():
+        col = np.array([448.0, -1.0, 0.5, 3 * 2.0 ** -9], dtype=np.float32) * np.float32(0.25)
+        q, sc = oracle.quantize_e4m3(wl.f32_to_bf16_bits(col.reshape(4, 1)), lib=lib)
+        return sc[0] == 0.25 and list(q[:, 0]) == [0x7E, 0xB8, 0x30, 0x03]
+
+    check("quantize_grid", quant_grid)
+    check("dequantize", lambda: np.array_equal(
+        oracle.dequantize_e4m3(np.array([[0x7E], [0xB8]], dtype=np.uint8),
+                               np.array([0.25], dtype=np.float32), lib=lib),
+        np.array([[112.0], [-0.25]])))
+
+    def f64_path():
+        inp = wl.random_inputs(12, 2, 16, 8, wl.BF16)
+        f = {k: wl.bf16_bits_to_f32(v).astype(np.float64) for k, v in inp.items()}
+        return np.array_equal(oracle.swiglu(f["x"], f["wg"], f["wu"], lib=lib),
+                              oracle.swiglu(inp["x"], inp["wg"], inp["wu"], lib=lib))
+
+    check("f64_path", f64_path)
     check("silu_log3", lambda: abs(oracle.silu(np.log(3.0), lib=lib) - np.log(3.0) * 0.75) < 1e-15)
     for dtype in (wl.F32, wl.BF16):
         inp = wl.integer_inputs(5, 3, 37, 29, dtype, with_down=True, lo=-3, hi=3)
