@@ -77,7 +77,7 @@ class Runner:
         t0 = time.time()
         self.inp = wl.make_inputs(w, M=w.M)
         log("inputs for %s generated in %.1fs" % (w.name, time.time() - t0))
-        tdt = torch.int16 if w.dtype == wl.BF16 else torch.float32
+        tdt = torch.float32 if w.dtype == wl.F32 else torch.int16
 
         def dev(a):
             a = np.ascontiguousarray(a)
@@ -180,7 +180,7 @@ PATH_NAMES = {1: "skinny", 2: "wide", 3: "wide-phased"}
 def dominant_kernel(w: wl.Workload, path: int) -> str:
     if path in (2, 3):
         return "wide_bf16_kernel"
-    return "skinny_bf16_kernel" if w.dtype == wl.BF16 else "skinny_f32_kernel"
+    return "skinny_f32_kernel" if w.dtype == wl.F32 else "skinny_bf16_kernel"
 
 
 def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0,
@@ -218,9 +218,15 @@ def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float) -> dict:
     import oracle
     threads = oracle.available_cores()
     x = inp["x"][:w.M]
+    if w.dtype == wl.FP8W:   # quantised once, outside the timing
+        q = {k: oracle.quantize_e4m3(inp[k]) for k in ("wg", "wu", "wd") if k in inp}
     reps, t0 = 0, time.perf_counter()
     while True:
-        if w.with_down:
+        if w.dtype == wl.FP8W and w.with_down:
+            oracle.mlp_fp8w(x, *q["wg"], *q["wu"], *q["wd"], nthreads=threads)
+        elif w.dtype == wl.FP8W:
+            oracle.swiglu_fp8w(x, *q["wg"], *q["wu"], nthreads=threads)
+        elif w.with_down:
             oracle.mlp(x, inp["wg"], inp["wu"], inp["wd"], nthreads=threads)
         else:
             oracle.swiglu(x, inp["wg"], inp["wu"], nthreads=threads)
@@ -291,7 +297,7 @@ def main() -> int:
     if args.probe:
         return probe()
     w = wl.WORKLOADS[args.workload]
-    one_copy = 2 * w.d * w.dff * w.elem_bytes
+    one_copy = 2 * w.d * w.dff * w.weight_bytes
     copies = max(1, -(-(1 << 30) // one_copy)) if one_copy < (1 << 30) else 1
     log("workload %s: %s, %d weight copies" % (w.name, w, copies))
     m = measure(w, args.steps, args.warmup, copies, PATHS[args.path], args.graph)
@@ -308,7 +314,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
+        "dtype": wl.DTYPE_NAMES[w.dtype],
         "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights, bf16 RNE)",
         "config": {"workload": w.name, "M": w.M, "d": w.d, "dff": w.dff,
                    "with_down": w.with_down, "path": PATH_NAMES[m["path"]],

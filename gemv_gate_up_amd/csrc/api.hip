@@ -35,11 +35,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_sizes(int64_t M, int64_t d, int64_t dff, int dtype)
 {
-    if (dtype != SWIGLU_F32 && dtype != SWIGLU_BF16)
+    if (dtype != SWIGLU_F32 && dtype != SWIGLU_BF16 && dtype != SWIGLU_BF16_FP8W)
         return SWIGLU_ERR_UNSUPPORTED;
     if (M < 0 || d <= 0 || dff <= 0)
         return SWIGLU_ERR_INVALID_ARG;
-    const int ve = vec_elems(dtype);
+    const int ve = act_vec_elems(dtype);
     if (d % ve != 0 || dff % ve != 0 || d > MAX_DIM || dff > MAX_DIM || M > MAX_M)
         return SWIGLU_ERR_UNSUPPORTED;
     return SWIGLU_OK;

@@ -23,22 +23,37 @@
 // Padding: K is rounded up to a multiple of KALIGN (two chunks) and the
 // number of pair blocks up to a multiple of PB_ALIGN; padded weights are
 // zero, so padded products are exactly zero.
+//
+// FP8 weights (DT_FP8W: OCP E4M3 codes, bf16 activations and outputs): a
+// lane's 16 bytes are 16 codes of one column, the 8 K values of its k-group
+// in each of two consecutive 32-K chunks (bytes 0-7: k0 + g*8 + 0..7,
+// bytes 8-15: k0 + 32 + g*8 + 0..7), so one piece covers 16 columns by 64 K
+// and widens into the B operands of two bf16 MFMAs.  K is padded to 64.
+// After the pieces comes one fp32 scale per packed column, ordered
+// [pair block][half][16] (entry 32p + 16h + c), zero for padded columns.
 #pragma once
 #include <stdint.h>
 
 namespace swg {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8W = 2 };
 enum : int { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 
 constexpr int PIECE_BYTES = 1024;
 constexpr int PIECE_VECS = 64;     // 16-byte vectors per piece
 constexpr int PB_ALIGN = 8;        // pair blocks: multiple of 8 (256 packed columns)
 
+// Activation (x, h, out, y) element size and 16-byte vector width: bf16 for
+// both the bf16 and the FP8-weight types.
 __host__ __device__ constexpr inline int elem_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
-__host__ __device__ constexpr inline int vec_elems(int dt) { return dt == DT_F32 ? 4 : 8; }
-__host__ __device__ constexpr inline int chunk_k(int dt) { return 4 * vec_elems(dt); }
-__host__ __device__ constexpr inline int k_align(int dt) { return 2 * chunk_k(dt); }
+__host__ __device__ constexpr inline int act_vec_elems(int dt) { return dt == DT_F32 ? 4 : 8; }
+// K covered by one piece, and the K padding.
+__host__ __device__ constexpr inline int chunk_k(int dt) {
+    return dt == DT_F32 ? 16 : (dt == DT_BF16 ? 32 : 64);
+}
+__host__ __device__ constexpr inline int k_align(int dt) {
+    return dt == DT_FP8W ? 64 : 2 * chunk_k(dt);
+}
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
@@ -53,7 +68,12 @@ struct PackGeom {
     int64_t npb_valid;  // pair blocks that hold real columns
     int cols_per_pb;    // output columns per pair block (16 or 32)
     int dt;
-    __host__ __device__ int64_t bytes() const { return npb * nkc * 2 * PIECE_BYTES; }
+    __host__ __device__ int64_t piece_bytes() const { return npb * nkc * 2 * PIECE_BYTES; }
+    // FP8 weights: the column scales follow the pieces
+    __host__ __device__ int64_t scale_offset() const { return piece_bytes(); }
+    __host__ __device__ int64_t bytes() const {
+        return piece_bytes() + (dt == DT_FP8W ? npb * 32 * 4 : 0);
+    }
     // output row width when the result is kept padded (workspace h)
     __host__ __device__ int64_t padded_cols() const { return npb * cols_per_pb; }
 };

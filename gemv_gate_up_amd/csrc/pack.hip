@@ -6,6 +6,12 @@
 // columns; the down packer lays Wdown out in the same piece format so that
 // the same kernels stream it.  Packing is a pure bit permutation (no
 // arithmetic): each output element is one input element or zero padding.
+//
+// FP8 weights are quantised while packing, column by column (the scheme is
+// stated with the DT_FP8W layout): a first pass finds each column's largest
+// magnitude and stores scale = amax / 448, a second pass writes the codes of
+// w / scale.  Both divisions are IEEE fp32 (__fdiv_rn) and the encoding is
+// exact integer arithmetic, so the codes are fully determined by the input.
 #include "device_common.h"
 #include "launch.h"
 
@@ -44,9 +50,95 @@ pack_kernel(const T* __restrict__ src0, const T* __restrict__ src1, T* __restric
         out[e] = vals[e];
 }
 
+// Column of a packed slot (pair block pb, half h, column c of the half) and
+// the source matrix that holds it.
+__device__ __forceinline__ int64_t packed_col(int64_t pb, int h, int c, int plain) {
+    return plain ? pb * 32 + h * 16 + c : pb * 16 + c;
+}
+
+// One thread per packed column slot: scale = max_k |w[k][n]| / 448.
+__global__ void __launch_bounds__(256)
+fp8_scale_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1,
+                 float* __restrict__ scales, int64_t K, int64_t N, int64_t slots, int plain)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= slots)
+        return;
+    const int64_t pb = t / 32;
+    const int h = (int)((t / 16) % 2), c = (int)(t % 16);
+    const int64_t n = packed_col(pb, h, c, plain);
+    const uint16_t* src = (plain || h == 0) ? src0 : src1;
+    float amax = 0.f;
+    if (n < N)
+        for (int64_t k = 0; k < K; ++k)
+            amax = fmaxf(amax, fabsf(bf16_to_f32(src[k * N + n])));
+    scales[t] = __fdiv_rn(amax, 448.0f);
+}
+
+// E4M3 code of v: nearest value, ties to the even code, saturating at 448.
+//   |v| >= 448            -> 0x7E (S.1111.110)
+//   |v| <  2^-6           -> subnormal code round(|v| * 2^9), 0..8 (8 is 2^-6)
+//   otherwise             -> keep 3 of fp32's 23 mantissa bits, rounding the
+//                            other 20 to nearest even (a carry moves into the
+//                            exponent), and rebias the exponent from 127 to 7
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return 0x7Fu;                              // NaN stays NaN
+    if (a >= 0x43E00000u)                          // 448.0f
+        return sign | 0x7Eu;
+    if (a < 0x3C800000u)                           // 2^-6
+        return sign | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+// One thread per 16-byte vector of the FP8 pieces.
+__global__ void __launch_bounds__(256)
+pack_fp8_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1,
+                const float* __restrict__ scales, i32x4* __restrict__ dst, int64_t K, int64_t N,
+                int64_t nkc, int64_t total_vecs, int plain)
+{
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= total_vecs)
+        return;
+    const int lane = (int)(v % PIECE_VECS);
+    const int64_t piece = v / PIECE_VECS;
+    const int h = (int)(piece % 2);
+    const int64_t kc = (piece / 2) % nkc;
+    const int64_t pb = piece / (2 * nkc);
+    const int c = lane % 16, g = lane / 16;
+    const int64_t n = packed_col(pb, h, c, plain);
+    const uint16_t* src = (plain || h == 0) ? src0 : src1;
+    const float s = scales[pb * 32 + h * 16 + c];
+    uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int64_t k = kc * 64 + (e < 8 ? g * 8 + e : 32 + g * 8 + (e - 8));
+        uint32_t code = 0u;
+        if (s != 0.f && k < K && n < N)
+            code = e4m3_code(__fdiv_rn(bf16_to_f32(src[k * N + n]), s));
+        word[e / 4] |= code << (8 * (e % 4));
+    }
+    dst[v] = i32x4{(int)word[0], (int)word[1], (int)word[2], (int)word[3]};
+}
+
 hipError_t launch_pack(const void* src0, const void* src1, void* dst, const PackGeom& g,
                        int plain, hipStream_t s)
 {
+    if (g.dt == DT_FP8W) {
+        float* scales = (float*)((uint8_t*)dst + g.scale_offset());
+        const int64_t slots = g.npb * 32;
+        fp8_scale_kernel<<<dim3((unsigned)ceil_div(slots, 256)), dim3(256), 0, s>>>(
+            (const uint16_t*)src0, (const uint16_t*)src1, scales, g.K, g.N, slots, plain);
+        const int64_t total = g.npb * g.nkc * 2 * PIECE_VECS;
+        pack_fp8_kernel<<<dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s>>>(
+            (const uint16_t*)src0, (const uint16_t*)src1, scales, (i32x4*)dst, g.K, g.N, g.nkc,
+            total, plain);
+        return hipGetLastError();
+    }
     int64_t total_vecs = g.npb * g.nkc * 2 * PIECE_VECS;
     int64_t blocks = ceil_div(total_vecs, 256);
     if (g.dt == DT_F32)

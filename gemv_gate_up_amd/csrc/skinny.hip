@@ -19,6 +19,11 @@
 // activations as the 16-row A operand: at M <= 16 the matrix unit has spare
 // throughput, and above M = 4 plain fp32 FMA on the VALU would take longer
 // than streaming the weights.  fp32 weights use VALU FMA.
+//
+// FP8 weights (W8) halve the streamed bytes: each 16-byte load brings 16
+// E4M3 codes that widen exactly to bf16 (every E4M3 value is a bf16 value)
+// with gfx950's packed conversion, feeding two MFMAs over two 32-K chunks;
+// the per-column scale multiplies the finished fp32 sum.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,18 +32,32 @@ namespace swg {
 constexpr int SK_WAVES = 4;
 constexpr int SK_THREADS = SK_WAVES * 64;
 
+// Eight E4M3 codes (two dwords, lowest byte first) -> eight bf16 values in
+// the same order; exact.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(int lo, int hi) {
+    i32x4 r;
+    r.x = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    r.y = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    r.z = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    r.w = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 // ---------------------------------------------------------------- bf16 (MFMA)
 // Each wave covers NPB consecutive pair blocks, so one activation fragment
 // (MT 16-row tiles of x over a 32-K chunk) feeds 2*NPB*MT MFMAs; with 16 or
 // more rows, re-reading that fragment per pair block would cost half as many
-// bytes again as the weights.
-template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT>
+// bytes again as the weights.  With W8 a piece spans two chunks (CH = 2),
+// so each step loads two activation fragments per row tile.
+template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT, bool W8>
 __global__ void __launch_bounds__(SK_THREADS)
 skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                    const i32x4* __restrict__ w, int64_t nkc, int64_t cps,
                    OutT* __restrict__ out, int64_t ldo, int64_t ncols_out,
-                   float* __restrict__ partial, int64_t npc, int M)
+                   float* __restrict__ partial, int64_t npc, int M,
+                   const float* __restrict__ scales)
 {
+    constexpr int CH = W8 ? 2 : 1;   // 32-K chunks per piece
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t pb0 = (int64_t)blockIdx.x * NPB;
@@ -77,33 +96,47 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                 }
             }
         }
-        i32x4 xa[U][MT];
+        i32x4 xa[U][CH][MT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t kc = kb + SK_WAVES * u;
-            const int64_t k = kc * 32 + akoff;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int row = rbase + mt * 16 + arow;
-                if (kc < kend && row < M && k < kvalid)
-                    xa[u][mt] = *(const i32x4*)(a + (int64_t)row * lda + k);
-                else
-                    xa[u][mt] = i32x4{0, 0, 0, 0};
+            for (int ch = 0; ch < CH; ++ch) {
+                const int64_t k = (kc * CH + ch) * 32 + akoff;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int row = rbase + mt * 16 + arow;
+                    if (kc < kend && row < M && k < kvalid)
+                        xa[u][ch][mt] = *(const i32x4*)(a + (int64_t)row * lda + k);
+                    else
+                        xa[u][ch][mt] = i32x4{0, 0, 0, 0};
+                }
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int p = 0; p < NPB; ++p) {
-                const bf16x8 bg = __builtin_bit_cast(bf16x8, wg[p][u]);
-                const bf16x8 bu = __builtin_bit_cast(bf16x8, wu[p][u]);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, xa[u][mt]);
-                    accg[p][mt] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, accg[p][mt], 0, 0, 0);
-                    accu[p][mt] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, accu[p][mt], 0, 0, 0);
+                for (int ch = 0; ch < CH; ++ch) {
+                    bf16x8 bg, bu;
+                    if constexpr (W8) {
+                        bg = ch == 0 ? e4m3x8_to_bf16(wg[p][u].x, wg[p][u].y)
+                                     : e4m3x8_to_bf16(wg[p][u].z, wg[p][u].w);
+                        bu = ch == 0 ? e4m3x8_to_bf16(wu[p][u].x, wu[p][u].y)
+                                     : e4m3x8_to_bf16(wu[p][u].z, wu[p][u].w);
+                    } else {
+                        bg = __builtin_bit_cast(bf16x8, wg[p][u]);
+                        bu = __builtin_bit_cast(bf16x8, wu[p][u]);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const bf16x8 av = __builtin_bit_cast(bf16x8, xa[u][ch][mt]);
+                        accg[p][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, accg[p][mt],
+                                                                               0, 0, 0);
+                        accu[p][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, accu[p][mt],
+                                                                               0, 0, 0);
+                    }
                 }
             }
         }
@@ -130,6 +163,9 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
             }
         }
         __syncthreads();
+        // column scales of the FP8 weights: entry 32 * pb + 16 * half + c
+        const float gs = W8 ? scales[pb * 32 + c] : 1.f;
+        const float us = W8 ? scales[pb * 32 + 16 + c] : 1.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             float g = 0.f, u = 0.f;
@@ -137,6 +173,10 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
             for (int wv = 0; wv < SK_WAVES; ++wv) {
                 g += red[wv][mt][0][src];
                 u += red[wv][mt][1][src];
+            }
+            if (W8) {
+                g *= gs;
+                u *= us;
             }
             const int row = rbase + mt * 16 + r;
             if (row >= M)
@@ -316,8 +356,8 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
 {
     SkinnyPlan p;
     p.grid_pb = ceil_div(g.ncols_out, g.geom.cols_per_pb);
-    p.pb_per_wg = g.dt == DT_BF16 ? bf16_pair_blocks(g.M) : 1;
-    p.row_tile = g.dt == DT_BF16 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M);
+    p.pb_per_wg = g.dt != DT_F32 ? bf16_pair_blocks(g.M) : 1;
+    p.row_tile = g.dt != DT_F32 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M);
     p.row_groups = ceil_div(g.M, p.row_tile);
     // Split K only when there are too few pair blocks (units of weight
     // streaming) to keep every CU busy; two pair blocks per workgroup are
@@ -340,44 +380,47 @@ size_t skinny_partial_bytes(const GemmArgs& g, const SkinnyPlan& p)
     return (size_t)p.splits * (size_t)g.M * (size_t)(g.geom.npb * 32) * sizeof(float);
 }
 
-template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT>
+template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT, bool W8>
 static void go_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     // With two pair blocks per workgroup and an odd count, the last
     // workgroup's second pair block is padding (zero weights, never stored):
     // the packed buffer holds a multiple of 8 pair blocks.
     dim3 grid((unsigned)ceil_div(p.grid_pb, NPB), (unsigned)p.splits, (unsigned)p.row_groups);
-    skinny_bf16_kernel<MT, U, NPB, EPI, SPLIT, OutT><<<grid, dim3(SK_THREADS), 0, s>>>(
+    const float* scales =
+        W8 ? (const float*)((const uint8_t*)g.w + g.geom.scale_offset()) : nullptr;
+    skinny_bf16_kernel<MT, U, NPB, EPI, SPLIT, OutT, W8><<<grid, dim3(SK_THREADS), 0, s>>>(
         (const uint16_t*)g.a, g.lda, g.geom.K, (const i32x4*)g.w, g.geom.nkc, p.chunks_per_split,
-        (OutT*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M);
+        (OutT*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M, scales);
 }
 
-template <int MT, int U, int NPB, int EPI>
+template <int MT, int U, int NPB, int EPI, bool W8>
 static void pick_split_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     if (p.splits > 1)
-        go_bf16<MT, U, NPB, EPI, true, uint16_t>(g, p, partial, s);
+        go_bf16<MT, U, NPB, EPI, true, uint16_t, W8>(g, p, partial, s);
     else
-        go_bf16<MT, U, NPB, EPI, false, uint16_t>(g, p, partial, s);
+        go_bf16<MT, U, NPB, EPI, false, uint16_t, W8>(g, p, partial, s);
 }
 
 // Loads in flight per lane: 2*NPB*U weight pieces plus U*MT activation
-// fragments (measured on the 8B- and 72B-class decode shapes).
-template <int EPI>
+// fragments (times two with FP8 weights), measured on the 8B- and
+// 72B-class decode shapes.
+template <int EPI, bool W8>
 static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     switch (p.row_tile / 16) {
     case 1:
         if (p.pb_per_wg == 2)
-            pick_split_bf16<1, 4, 2, EPI>(g, p, partial, s);
+            pick_split_bf16<1, 4, 2, EPI, W8>(g, p, partial, s);
         else if (g.M > 4)
-            pick_split_bf16<1, 4, 1, EPI>(g, p, partial, s);
+            pick_split_bf16<1, 4, 1, EPI, W8>(g, p, partial, s);
         else
-            pick_split_bf16<1, 8, 1, EPI>(g, p, partial, s);
+            pick_split_bf16<1, 8, 1, EPI, W8>(g, p, partial, s);
         break;
-    case 2: pick_split_bf16<2, 4, 2, EPI>(g, p, partial, s); break;
-    case 3: pick_split_bf16<3, 2, 2, EPI>(g, p, partial, s); break;
-    default: pick_split_bf16<4, 2, 2, EPI>(g, p, partial, s); break;
+    case 2: pick_split_bf16<2, 4, 2, EPI, W8>(g, p, partial, s); break;
+    case 3: pick_split_bf16<3, 2, 2, EPI, W8>(g, p, partial, s); break;
+    default: pick_split_bf16<4, 2, 2, EPI, W8>(g, p, partial, s); break;
     }
 }
 
@@ -423,9 +466,14 @@ hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial,
 {
     if (g.dt == DT_BF16) {
         if (g.epi == EPI_SWIGLU)
-            pick_mt_bf16<EPI_SWIGLU>(g, p, partial, s);
+            pick_mt_bf16<EPI_SWIGLU, false>(g, p, partial, s);
         else
-            pick_mt_bf16<EPI_PLAIN>(g, p, partial, s);
+            pick_mt_bf16<EPI_PLAIN, false>(g, p, partial, s);
+    } else if (g.dt == DT_FP8W) {
+        if (g.epi == EPI_SWIGLU)
+            pick_mt_bf16<EPI_SWIGLU, true>(g, p, partial, s);
+        else
+            pick_mt_bf16<EPI_PLAIN, true>(g, p, partial, s);
     } else {
         if (g.epi == EPI_SWIGLU)
             pick_rt_f32<EPI_SWIGLU>(g, p, partial, s);
@@ -435,7 +483,7 @@ hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits <= 1)
         return e;
-    if (g.dt == DT_BF16) {
+    if (g.dt != DT_F32) {
         if (g.epi == EPI_SWIGLU)
             go_reduce<EPI_SWIGLU, uint16_t>(g, p, partial, s);
         else

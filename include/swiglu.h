@@ -19,8 +19,9 @@
  *     this header are the one exception: they keep the pointers they were
  *     captured with).
  *   - dtype is SWIGLU_BF16 (bf16 storage, fp32 accumulation, bf16 output)
- *     or SWIGLU_F32 (fp32 storage and arithmetic).  x, the weights and the
- *     output share one dtype.
+ *     or SWIGLU_F32 (fp32 storage and arithmetic): x, the weights and the
+ *     output share that dtype.  Or SWIGLU_BF16_FP8W: x, out and y in bf16,
+ *     weights stored as 8-bit floats (see below), fp32 accumulation.
  *   - Calls only enqueue kernels on `stream` (the graph-creation calls
  *     excepted): no allocation, no copy, no
  *     synchronisation (the decode-path conventions of "Où part le temps d'un
@@ -51,7 +52,24 @@ extern "C" {
 
 typedef enum swiglu_dtype {
     SWIGLU_F32 = 0,
-    SWIGLU_BF16 = 1
+    SWIGLU_BF16 = 1,
+    /*
+     * FP8 weights for decode: "Tile-Level Activation Overlap for Efficient
+     * LLM Inference" (section on the problem) notes that quantised weights
+     * make the memory-bound part weigh more; streaming one byte per weight
+     * halves the decode path's traffic.  The pack calls take bf16 Wgate,
+     * Wup and Wdown and quantise each output column: scale = (largest
+     * magnitude in the column) / 448 in fp32, codes = OCP E4M3 (no
+     * infinities; largest value 448) nearest to w / scale (an fp32
+     * division), ties to the even code, saturating; an all-zero column
+     * gets scale 0.  The kernels widen the codes exactly to bf16, multiply
+     * on the matrix unit with fp32 accumulation and apply the column scale
+     * to the finished sum.  Served by the skinny path only (any M; it is
+     * built for M <= 64): SWIGLU_PATH_WIDE and WIDE_PHASED return
+     * SWIGLU_ERR_UNSUPPORTED.  The packed buffers hold the codes (one byte
+     * per weight, padded like bf16) followed by the fp32 column scales.
+     */
+    SWIGLU_BF16_FP8W = 2
 } swiglu_dtype_t;
 
 typedef enum swiglu_status {
@@ -114,7 +132,9 @@ int swiglu_select_path(int64_t M, int64_t d, int64_t dff, int dtype);
  * Packs Wgate and Wup (each d x dff, row-major, device) into Wpacked (device,
  * swiglu_packed_bytes(d, dff, dtype) bytes).  Done once per weight set; the
  * packed buffer then serves every M and both paths.  Pure permutation with
- * zero padding: no rounding.  Wpacked must not overlap Wgate or Wup.
+ * zero padding: no rounding (SWIGLU_BF16_FP8W: Wgate and Wup are bf16 and
+ * are quantised as described with that dtype).  Wpacked must not overlap
+ * Wgate or Wup.
  */
 int swiglu_pack_weights(const void *Wgate, const void *Wup, void *Wpacked,
                         int64_t d, int64_t dff, int dtype, hipStream_t stream);

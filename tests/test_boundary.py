@@ -143,3 +143,23 @@ def test_one_hip_runtime_in_the_process():
     maps = open("/proc/self/maps").read().split("\n")
     files = {line.split()[-1] for line in maps if "libamdhip64" in line}
     assert len(files) == 1, files
+
+
+def test_fp8_weight_sizes_and_paths():
+    W8 = sw.SWIGLU_BF16_FP8W
+    # one byte per weight, K padded to 64, then one fp32 scale per packed column
+    assert sw.swiglu_packed_bytes(4096, 14336, W8) == 4096 * 14336 * 2 + 896 * 32 * 4
+    # K 104 -> 128; 40 columns -> 3 pair blocks -> 8 (128 packed columns per half)
+    assert sw.swiglu_packed_bytes(104, 40, W8) == 128 * 128 * 2 + 8 * 32 * 4
+    assert sw.swiglu_packed_bytes(100, 40, W8) == 0
+    assert sw.swiglu_down_packed_bytes(8192, 29568, W8) == 29568 * 8192 + 256 * 32 * 4
+    for M in (1, 64, 65, 4096):
+        assert sw.swiglu_select_path(M, 4096, 14336, W8) == sw.SWIGLU_PATH_SKINNY
+    for path in (sw.SWIGLU_PATH_WIDE, sw.SWIGLU_PATH_WIDE_PHASED):
+        rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, W8, None, 0, 0, path)
+        assert rc == sw.SWIGLU_ERR_UNSUPPORTED
+    # activations stay bf16: d and dff multiples of 8
+    assert sw.swiglu_up(FAKE, FAKE, FAKE, 1, 68, 64, W8, None, 0, stream=0) == \
+        sw.SWIGLU_ERR_UNSUPPORTED
+    # the down product's h is bf16 in the workspace, like the bf16 dtype
+    assert sw.swiglu_workspace_bytes(16, 8192, 29568, W8, 1) >= 16 * 29568 * 2

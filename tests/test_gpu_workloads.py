@@ -63,6 +63,26 @@ def test_mlp_workload(name):
     say(name, st)
 
 
+@pytest.mark.parametrize("name", ["decode8b_m1_fp8w", "decode8b_m16_fp8w", "mlp72b_m16_fp8w"])
+def test_fp8w_workload(name):
+    # FP8 weights at the decode shapes: reference = the oracle's product with
+    # the oracle's own quantisation of the same bf16 weights (the packer's
+    # codes equal it bit for bit: test_gpu_fp8w.py)
+    w = wl.WORKLOADS[name]
+    say("workload", name, w)
+    inp = wl.make_inputs(w, M=w.M)
+    wp, wdp = pack(inp, w.d, w.dff, w.dtype)
+    q = {k: oracle.quantize_e4m3(inp[k]) for k in ("wg", "wu", "wd") if k in inp}
+    if w.with_down:
+        out = run_mlp(dev(inp["x"]), wp, wdp, w.M, w.d, w.dff, w.dtype)
+        ref = oracle.mlp_fp8w(inp["x"], *q["wg"], *q["wu"], *q["wd"])
+    else:
+        out = run_up(dev(inp["x"]), wp, w.M, w.d, w.dff, w.dtype)
+        ref = oracle.swiglu_fp8w(inp["x"], *q["wg"], *q["wu"])
+    st = assert_close(host(out, w.dtype), ref, w.dtype, name)
+    say(name, st)
+
+
 def test_mlp72b_tensor_parallel_shard():
     # One GPU's share of the 72B-class MLP split eight ways over d_ff
     # (29568 / 8 = 3696 columns, not a multiple of the 128-column tile).

@@ -19,7 +19,8 @@ import numpy as np
 
 F32 = 0
 BF16 = 1
-DTYPE_NAMES = {F32: "f32", BF16: "bf16"}
+FP8W = 2     # bf16 activations; weights packed as E4M3 codes (drawn here in bf16)
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8W: "bf16-fp8w"}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -30,20 +31,29 @@ class Workload:
     M: int
     d: int
     dff: int
-    dtype: int          # F32 or BF16
+    dtype: int          # F32, BF16 or FP8W
     with_down: bool     # full MLP (gate/up + down projection) or up only
     m_max: int          # rows drawn for x; smaller M take the leading rows
 
     @property
     def elem_bytes(self) -> int:
+        """Bytes per activation element (x, out, y)."""
         return 4 if self.dtype == F32 else 2
 
+    @property
+    def weight_bytes(self) -> int:
+        """Bytes per stored weight."""
+        return 1 if self.dtype == FP8W else self.elem_bytes
+
     def algorithmic_bytes(self) -> int:
-        """Bytes the method must move: weights once, x once, output once."""
-        s = self.elem_bytes
-        b = 2 * self.d * self.dff * s + self.M * self.d * s
+        """Bytes the method must move: weights once (with their fp32 column
+        scales when stored as FP8), x once, output once."""
+        s, ws = self.elem_bytes, self.weight_bytes
+        b = 2 * self.d * self.dff * ws + self.M * self.d * s
+        if self.dtype == FP8W:
+            b += 2 * self.dff * 4 + (self.d * 4 if self.with_down else 0)
         if self.with_down:
-            b += self.dff * self.d * s + self.M * self.d * s
+            b += self.dff * self.d * ws + self.M * self.d * s
         else:
             b += self.M * self.dff * s
         return b
@@ -70,6 +80,11 @@ WORKLOADS = {
     "prefill8b_m4096": _wl(4, "prefill8b_m4096", 4096, 4096, 14336, BF16, False, 4096),
     "mlp72b_m16": _wl(5, "mlp72b_m16", 16, 8192, 29568, BF16, True, 2048),
     "mlp72b_m2048": _wl(5, "mlp72b_m2048", 2048, 8192, 29568, BF16, True, 2048),
+    # the decode shapes with FP8 weights (same seeds, so the same bf16
+    # weights before quantisation)
+    "decode8b_m1_fp8w": _wl(2, "decode8b_m1_fp8w", 1, 4096, 14336, FP8W, False, 16),
+    "decode8b_m16_fp8w": _wl(2, "decode8b_m16_fp8w", 16, 4096, 14336, FP8W, False, 16),
+    "mlp72b_m16_fp8w": _wl(5, "mlp72b_m16_fp8w", 16, 8192, 29568, FP8W, True, 2048),
 }
 
 # tensor ids used in seeds: seed = 1000 * cfg + id
@@ -103,7 +118,8 @@ def normal(seed: int, shape, std: float) -> np.ndarray:
 
 
 def to_storage(a32: np.ndarray, dtype: int) -> np.ndarray:
-    """fp32 array -> storage array: float32 as is, or uint16 bf16 bits."""
+    """fp32 array -> storage array: float32 as is, or uint16 bf16 bits (also
+    for FP8W, whose weights are quantised by the packer)."""
     if dtype == F32:
         return np.ascontiguousarray(a32, dtype=np.float32)
     return f32_to_bf16_bits(a32)
