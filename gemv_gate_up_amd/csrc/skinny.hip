@@ -343,9 +343,10 @@ static int bf16_row_tiles(int64_t M) {
 }
 
 // Pair blocks per wave of the bf16 kernel: two once x's fragment is as large
-// as a weight piece (more than 8 rows), one otherwise.
-static int bf16_pair_blocks(int64_t M) {
-    return M > 8 ? 2 : 1;
+// as a weight piece (more than 8 rows), one otherwise.  FP8 weights always
+// take two (measured best at 1, 8 and 16 rows on the 8B and 72B shapes).
+static int bf16_pair_blocks(int64_t M, int dt) {
+    return (dt == DT_FP8W || M > 8) ? 2 : 1;
 }
 
 static int f32_row_tile(int64_t M) {
@@ -356,7 +357,7 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
 {
     SkinnyPlan p;
     p.grid_pb = ceil_div(g.ncols_out, g.geom.cols_per_pb);
-    p.pb_per_wg = g.dt != DT_F32 ? bf16_pair_blocks(g.M) : 1;
+    p.pb_per_wg = g.dt != DT_F32 ? bf16_pair_blocks(g.M, g.dt) : 1;
     p.row_tile = g.dt != DT_F32 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M);
     p.row_groups = ceil_div(g.M, p.row_tile);
     // Split K only when there are too few pair blocks (units of weight
@@ -411,7 +412,9 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
 {
     switch (p.row_tile / 16) {
     case 1:
-        if (p.pb_per_wg == 2)
+        if (W8)   // a piece already spans 64 K: two in flight per half suffice
+            pick_split_bf16<1, 2, 2, EPI, W8>(g, p, partial, s);
+        else if (p.pb_per_wg == 2)
             pick_split_bf16<1, 4, 2, EPI, W8>(g, p, partial, s);
         else if (g.M > 4)
             pick_split_bf16<1, 4, 1, EPI, W8>(g, p, partial, s);
