@@ -245,7 +245,7 @@ def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float) -> dict:
 def probe() -> int:
     """Kernels for hardware-counter runs: a plain copy of known size (reads
     and writes exactly 1 GiB) to calibrate FETCH_SIZE / WRITE_SIZE, then the
-    decode and prefill steps as the bench runs them."""
+    decode (bf16 and FP8 weights) and prefill steps as the bench runs them."""
     import torch
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -255,9 +255,9 @@ def probe() -> int:
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
-    for name, steps in (("decode8b_m1", 5), ("prefill8b_m4096", 3)):
+    for name, steps in (("decode8b_m1", 5), ("decode8b_m1_fp8w", 5), ("prefill8b_m4096", 3)):
         w = wl.WORKLOADS[name]
-        r = Runner(w, 5 if name == "decode8b_m1" else 1)
+        r = Runner(w, 5 if w.M == 1 else 1)
         for i in range(steps):
             r.step(i)
         torch.cuda.synchronize()
