@@ -69,6 +69,8 @@ def _bind(lib):
     lib.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
     lib.oracle_quantize_e4m3_columns.restype = ctypes.c_int
     lib.oracle_quantize_e4m3_columns.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_rmsnorm_rows.restype = ctypes.c_int
+    lib.oracle_rmsnorm_rows.argtypes = [ctypes.c_int, vp, vp, ctypes.c_double, i64, i64, dp]
     lib.oracle_dequantize_e4m3_columns.restype = ctypes.c_int
     lib.oracle_dequantize_e4m3_columns.argtypes = [vp, vp, i64, i64, dp]
     return lib
@@ -212,6 +214,48 @@ def mlp_fp8w(x, qg, sg, qu, su, qd, sd, rows=None, nthreads=0, lib=None):
     return mlp(bf16_array_to_double(x, lib), dequantize_e4m3(qg, sg, lib),
                dequantize_e4m3(qu, su, lib), dequantize_e4m3(qd, sd, lib), rows=rows,
                nthreads=nthreads, lib=lib)
+
+
+def to_double(a, lib=None) -> np.ndarray:
+    """Exact fp64 copy of a storage array (float32, float64, or bf16 bits)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return bf16_array_to_double(a, lib)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError("float32, float64 or bf16 bits expected")
+
+
+def rmsnorm(r, gamma, eps, lib=None) -> np.ndarray:
+    """n = r / sqrt(mean(r^2) + eps) * gamma per row, in fp64."""
+    r = np.ascontiguousarray(r)
+    gamma = np.ascontiguousarray(gamma)
+    if _dtype_of(gamma) != _dtype_of(r):
+        raise TypeError("r and gamma must share one dtype")
+    M, d = r.shape
+    if gamma.shape != (d,):
+        raise ValueError("gamma must hold d values")
+    out = np.empty((M, d), dtype=np.float64)
+    rc = (lib or _load()).oracle_rmsnorm_rows(_dtype_of(r), _ptr(r), _ptr(gamma), float(eps), M, d,
+                                              _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_rmsnorm_rows failed")
+    return out
+
+
+def mlp_block(r, gamma, eps, wg, wu, wd, bias=None, rows=None, nthreads=0, lib=None):
+    """The MLP half of a pre-normalised layer ("Anatomie d'un transformeur
+    sur GPU" §1.1; kernels 7 to 11 of §1.6): out = r + MLP(rmsnorm(r)) (+ bias
+    on the down product, the Affine operation of "Où part le temps d'un
+    token").  Weights are storage arrays or fp64 (dequantised) arrays; the
+    normalised rows are not rounded.  fp64."""
+    n = rmsnorm(r, gamma, eps, lib=lib)
+    f = lambda a: to_double(a, lib)
+    y = mlp(n, f(wg), f(wu), f(wd), rows=rows, nthreads=nthreads, lib=lib)
+    if bias is not None:
+        y = y + f(bias)[None, :]
+    rr = f(r) if rows is None else f(r)[np.asarray(rows)]
+    return rr + y
 
 
 def default_threads() -> int:

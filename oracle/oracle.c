@@ -301,6 +301,33 @@ int oracle_mlp_rows(int dtype, const void *x, const void *wg, const void *wu,
     return rc;
 }
 
+/*
+ * RMSNorm of the rows of r (M x d): n[m][i] = r[m][i] / sqrt(ms + eps) *
+ * gamma[i], with ms = (1/d) sum_i r[m][i]^2 taken in ascending i.  The
+ * pre-normalisation of the MLP half of a layer ("Anatomie d'un
+ * transformeur sur GPU" §1.1 skeleton; §1.6 kernel 7); the pages do not
+ * write the formula out, this is the usual root-mean-square normalisation
+ * with a learned per-feature gain and a caller-given eps.  fp64 throughout.
+ */
+int oracle_rmsnorm_rows(int dtype, const void *r, const void *gamma, double eps, int64_t M,
+                        int64_t d, double *out)
+{
+    if ((dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64) || M < 0 ||
+        d <= 0 || !r || !gamma || !out || !(eps >= 0.0))
+        return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t i = 0; i < d; ++i) {
+            double v = elem(r, dtype, m * d + i);
+            ss += v * v;
+        }
+        double inv = 1.0 / sqrt(ss / (double)d + eps);
+        for (int64_t i = 0; i < d; ++i)
+            out[m * d + i] = elem(r, dtype, m * d + i) * inv * elem(gamma, dtype, i);
+    }
+    return 0;
+}
+
 /* Number of threads an nthreads=0 call would use (for reporting). */
 int oracle_default_threads(void)
 {

@@ -43,6 +43,12 @@ MUTANTS = {
                             "out[k * N + n] = oracle_e4m3_to_double"),
     "f64_read_as_f32": ("return ((const double *)p)[i];",
                         "return (double)((const float *)p)[i];"),
+    # RMSNorm
+    "rms_no_eps": ("sqrt(ss / (double)d + eps)", "sqrt(ss / (double)d)"),
+    "rms_sum_not_mean": ("sqrt(ss / (double)d + eps)", "sqrt(ss + eps)"),
+    "rms_no_sqrt": ("1.0 / sqrt(ss / (double)d + eps)", "1.0 / (ss / (double)d + eps)"),
+    "rms_no_gain": ("out[m * d + i] = elem(r, dtype, m * d + i) * inv * elem(gamma, dtype, i);",
+                    "out[m * d + i] = elem(r, dtype, m * d + i) * inv;"),
 }
 
 
@@ -88,6 +94,14 @@ def pin_failures(lib):
                               oracle.swiglu(inp["x"], inp["wg"], inp["wu"], lib=lib))
 
     check("f64_path", f64_path)
+    # RMSNorm: the hand-worked row [3, 4] (n = [0.6, 0.8] * sqrt 2), a gain,
+    # and the eps closed form at d = 1
+    check("rmsnorm_hand", lambda: np.allclose(
+        oracle.rmsnorm(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 0.0, lib=lib)[0],
+        [0.6 * np.sqrt(2), 1.6 * np.sqrt(2)], rtol=1e-15, atol=0))
+    check("rmsnorm_eps", lambda: abs(
+        oracle.rmsnorm(np.array([[0.3]]), np.array([1.0]), 1e-2, lib=lib)[0, 0]
+        - 0.3 / np.sqrt(0.09 + 1e-2)) < 1e-15)
     check("silu_log3", lambda: abs(oracle.silu(np.log(3.0), lib=lib) - np.log(3.0) * 0.75) < 1e-15)
     for dtype in (wl.F32, wl.BF16):
         inp = wl.integer_inputs(5, 3, 37, 29, dtype, with_down=True, lo=-3, hi=3)
