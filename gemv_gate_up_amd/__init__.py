@@ -81,6 +81,12 @@ _SIGS = {
     "mlp_forward_graph_create": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz,
                                         _int, ctypes.POINTER(_vp)]),
     "swiglu_graph_launch": (_int, [_vp, _vp]),
+    "mlp_block_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
+    "mlp_block_workspace_bytes_ex": (_sz, [_i64, _i64, _i64, _int, _int]),
+    "mlp_block_forward": (_int, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                 _int, _vp, _sz, _vp]),
+    "mlp_block_forward_ex": (_int, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _i64, _i64,
+                                    _i64, _int, _vp, _sz, _vp, _int]),
     "swiglu_graph_destroy": (_int, [_vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -172,6 +178,29 @@ def mlp_forward_ex(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace=None, wo
                    stream=None, path=SWIGLU_PATH_AUTO) -> int:
     return _lib.mlp_forward_ex(_ptr(x), _ptr(Wpacked), _ptr(Wdpacked), _ptr(y), M, d, dff,
                                dtype, _ptr(workspace), workspace_bytes, _stream(stream), path)
+
+
+def mlp_block_workspace_bytes(M, d, dff, dtype) -> int:
+    return _lib.mlp_block_workspace_bytes(M, d, dff, dtype)
+
+
+def mlp_block_workspace_bytes_ex(M, d, dff, dtype, path) -> int:
+    return _lib.mlp_block_workspace_bytes_ex(M, d, dff, dtype, path)
+
+
+def mlp_block_forward(r, gamma, eps, Wpacked, Wdpacked, bias, out, M, d, dff, dtype,
+                      workspace=None, workspace_bytes=0, stream=None) -> int:
+    return _lib.mlp_block_forward(_ptr(r), _ptr(gamma), eps, _ptr(Wpacked), _ptr(Wdpacked),
+                                  _ptr(bias), _ptr(out), M, d, dff, dtype, _ptr(workspace),
+                                  workspace_bytes, _stream(stream))
+
+
+def mlp_block_forward_ex(r, gamma, eps, Wpacked, Wdpacked, bias, out, M, d, dff, dtype,
+                         workspace=None, workspace_bytes=0, stream=None,
+                         path=SWIGLU_PATH_AUTO) -> int:
+    return _lib.mlp_block_forward_ex(_ptr(r), _ptr(gamma), eps, _ptr(Wpacked), _ptr(Wdpacked),
+                                     _ptr(bias), _ptr(out), M, d, dff, dtype, _ptr(workspace),
+                                     workspace_bytes, _stream(stream), path)
 
 
 def swiglu_up_graph_create(x, Wpacked, out, M, d, dff, dtype, workspace=None, workspace_bytes=0,

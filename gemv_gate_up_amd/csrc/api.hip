@@ -176,6 +176,32 @@ int do_up(const void* x, const void* wp, void* out, int64_t M, int64_t d, int64_
     return run(g, p, ws, s);
 }
 
+// Launches of the MLP on checked arguments: h = silu(x.Wg) * (x.Wu) into
+// the workspace, then y = h.Wd (+ bias) (+ resid).
+int run_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, int64_t d,
+            int64_t dff, int dtype, void* ws, hipStream_t s, int path, const void* resid,
+            const void* bias)
+{
+    GemmArgs u = up_args(M, d, dff, dtype, true);
+    GemmArgs dn = down_args(M, d, dff, dtype);
+    const int pu = resolve_path(u, path), pd = resolve_path(dn, path);
+    uint8_t* h = (uint8_t*)ws;
+    uint8_t* partial = h + h_bytes(M, d, dff, dtype);
+    u.a = x;
+    u.w = wp;
+    u.out = h;
+    int rc = run(u, pu, partial, s);
+    if (rc != SWIGLU_OK)
+        return rc;
+    dn.a = h;
+    dn.w = wdp;
+    dn.out = y;
+    dn.resid = resid;
+    dn.ldr = d;
+    dn.bias = bias;
+    return run(dn, pd, partial, s);
+}
+
 int do_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, int64_t d,
            int64_t dff, int dtype, void* ws, size_t ws_bytes, hipStream_t s, int path,
            bool launch = true)
@@ -203,18 +229,50 @@ int do_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, i
         return SWIGLU_ERR_WORKSPACE;
     if (!launch)
         return SWIGLU_OK;
-    uint8_t* h = (uint8_t*)ws;
-    uint8_t* partial = h + h_bytes(M, d, dff, dtype);
-    u.a = x;
-    u.w = wp;
-    u.out = h;
-    rc = run(u, pu, partial, s);
-    if (rc != SWIGLU_OK)
+    return run_mlp(x, wp, wdp, y, M, d, dff, dtype, ws, s, path, nullptr, nullptr);
+}
+
+// The MLP block: out = r + MLP(rmsnorm(r)) (+ bias).  Workspace: the
+// normalised rows n (M x d, activation type), then the MLP's workspace.
+size_t n_bytes(int64_t M, int64_t d, int dt) { return align_up((size_t)M * d * elem_bytes(dt)); }
+
+int64_t block_need(int64_t M, int64_t d, int64_t dff, int dt, int path)
+{
+    const int64_t mlp = workspace_need(M, d, dff, dt, 1, path);
+    return mlp < 0 ? mlp : (int64_t)n_bytes(M, d, dt) + mlp;
+}
+
+int do_block(const void* r, const void* gamma, float eps, const void* wp, const void* wdp,
+             const void* bias, void* out, int64_t M, int64_t d, int64_t dff, int dtype, void* ws,
+             size_t ws_bytes, hipStream_t s, int path, bool launch = true)
+{
+    int rc = check_sizes(M, d, dff, dtype);
+    if (rc == SWIGLU_OK)
+        rc = check_path(path);
+    if (rc != SWIGLU_OK || M == 0)
         return rc;
-    dn.a = h;
-    dn.w = wdp;
-    dn.out = y;
-    return run(dn, pd, partial, s);
+    if (!r || !gamma || !wp || !wdp || !out || !ws || !(eps >= 0.0f) || !(eps <= 3.4e38f))
+        return SWIGLU_ERR_INVALID_ARG;
+    if (!aligned16(r) || !aligned16(gamma) || !aligned16(wp) || !aligned16(wdp) ||
+        !aligned16(out) || !aligned16(ws) || ((uintptr_t)bias % elem_bytes(dtype)) != 0)
+        return SWIGLU_ERR_MISALIGNED;
+    GemmArgs u = up_args(M, d, dff, dtype, true);
+    GemmArgs dn = down_args(M, d, dff, dtype);
+    if (resolve_path(u, path) < 0)
+        return resolve_path(u, path);
+    if (resolve_path(dn, path) < 0)
+        return resolve_path(dn, path);
+    const int64_t need = block_need(M, d, dff, dtype, path);
+    if (need < 0)
+        return (int)need;
+    if ((size_t)need > ws_bytes)
+        return SWIGLU_ERR_WORKSPACE;
+    if (!launch)
+        return SWIGLU_OK;
+    uint8_t* n = (uint8_t*)ws;
+    if (launch_rmsnorm(r, gamma, eps, M, d, dtype, n, s) != hipSuccess)
+        return SWIGLU_ERR_HIP;
+    return run_mlp(n, wp, wdp, out, M, d, dff, dtype, n + n_bytes(M, d, dtype), s, path, r, bias);
 }
 
 // Records one call (`call(stream, launch)` returns a status) on a private
@@ -382,6 +440,37 @@ int mlp_forward_ex(const void* x, const void* Wpacked, const void* Wdpacked, voi
 {
     return do_mlp(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace, workspace_bytes, stream,
                   path);
+}
+
+size_t mlp_block_workspace_bytes_ex(int64_t M, int64_t d, int64_t dff, int dtype, int path)
+{
+    if (check_sizes(M, d, dff, dtype) != SWIGLU_OK || check_path(path) != SWIGLU_OK || M == 0)
+        return 0;
+    const int64_t need = block_need(M, d, dff, dtype, path);
+    return need < 0 ? 0 : (size_t)need;
+}
+
+size_t mlp_block_workspace_bytes(int64_t M, int64_t d, int64_t dff, int dtype)
+{
+    return mlp_block_workspace_bytes_ex(M, d, dff, dtype, SWIGLU_PATH_AUTO);
+}
+
+int mlp_block_forward(const void* r, const void* gamma, float eps, const void* Wpacked,
+                      const void* Wdpacked, const void* bias, void* out, int64_t M, int64_t d,
+                      int64_t dff, int dtype, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream)
+{
+    return do_block(r, gamma, eps, Wpacked, Wdpacked, bias, out, M, d, dff, dtype, workspace,
+                    workspace_bytes, stream, SWIGLU_PATH_AUTO);
+}
+
+int mlp_block_forward_ex(const void* r, const void* gamma, float eps, const void* Wpacked,
+                         const void* Wdpacked, const void* bias, void* out, int64_t M, int64_t d,
+                         int64_t dff, int dtype, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream, int path)
+{
+    return do_block(r, gamma, eps, Wpacked, Wdpacked, bias, out, M, d, dff, dtype, workspace,
+                    workspace_bytes, stream, path);
 }
 
 int swiglu_up_graph_create(const void* x, const void* Wpacked, void* out, int64_t M, int64_t d,

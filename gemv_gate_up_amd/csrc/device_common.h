@@ -35,6 +35,26 @@ __device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
+template <typename T>
+__device__ __forceinline__ float load_act(const T* p);
+template <>
+__device__ __forceinline__ float load_act<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_act<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// Epilogue additions of a plain product (the down projection of the MLP
+// block): the bias of the "Affine" operation, then the residual, both in
+// fp32 before the one rounding of the store.  Null pointers add nothing.
+template <typename T>
+__device__ __forceinline__ float plain_tail(float v, const T* resid, int64_t ldr, const T* bias,
+                                            int64_t row, int64_t col) {
+    if (bias)
+        v += load_act(bias + col);
+    if (resid)
+        v += load_act(resid + row * ldr + col);
+    return v;
+}
+
 // Buffer resource over [base, base + num_bytes): loads at offsets at or
 // past num_bytes return zero without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {

@@ -24,7 +24,16 @@ struct GemmArgs {
     int64_t M;
     int epi;            // EPI_SWIGLU or EPI_PLAIN
     int dt;
+    // EPI_PLAIN only, may be null: out = A.W (+ bias[col]) (+ resid[row][col])
+    const void* resid;  // M x ldr, activation type
+    int64_t ldr;
+    const void* bias;   // ncols_out values, activation type
 };
+
+// RMSNorm prologue (norm.hip): n = r / sqrt(mean(r^2) + eps) * gamma per
+// row; r, gamma and n in the activation type of dt.
+hipError_t launch_rmsnorm(const void* r, const void* gamma, float eps, int64_t M, int64_t d,
+                          int dt, void* n, hipStream_t s);
 
 // Split-K plan for the skinny kernels.
 struct SkinnyPlan {

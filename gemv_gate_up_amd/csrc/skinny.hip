@@ -55,7 +55,8 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                    const i32x4* __restrict__ w, int64_t nkc, int64_t cps,
                    OutT* __restrict__ out, int64_t ldo, int64_t ncols_out,
                    float* __restrict__ partial, int64_t npc, int M,
-                   const float* __restrict__ scales)
+                   const float* __restrict__ scales, const OutT* __restrict__ resid, int64_t ldr,
+                   const OutT* __restrict__ bias)
 {
     constexpr int CH = W8 ? 2 : 1;   // 32-K chunks per piece
     const int lane = threadIdx.x & 63;
@@ -192,9 +193,10 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
             } else {
                 const int64_t j = pb * 32 + c;
                 if (j < ncols_out)
-                    store_out(out + (int64_t)row * ldo + j, g);
+                    store_out(out + (int64_t)row * ldo + j, plain_tail(g, resid, ldr, bias, row, j));
                 if (j + 16 < ncols_out)
-                    store_out(out + (int64_t)row * ldo + j + 16, u);
+                    store_out(out + (int64_t)row * ldo + j + 16,
+                              plain_tail(u, resid, ldr, bias, row, j + 16));
             }
         }
     }
@@ -209,7 +211,8 @@ __global__ void __launch_bounds__(SK_THREADS)
 skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
                   const f32x4* __restrict__ w, int64_t nkc, int64_t cps,
                   OutT* __restrict__ out, int64_t ldo, int64_t ncols_out,
-                  float* __restrict__ partial, int64_t npc, int M)
+                  float* __restrict__ partial, int64_t npc, int M,
+                  const OutT* __restrict__ resid, int64_t ldr, const OutT* __restrict__ bias)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -302,9 +305,10 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
     } else {
         const int64_t j = pb * 32 + c;
         if (j < ncols_out)
-            store_out(out + (int64_t)row * ldo + j, g);
+            store_out(out + (int64_t)row * ldo + j, plain_tail(g, resid, ldr, bias, row, j));
         if (j + 16 < ncols_out)
-            store_out(out + (int64_t)row * ldo + j + 16, u);
+            store_out(out + (int64_t)row * ldo + j + 16,
+                      plain_tail(u, resid, ldr, bias, row, j + 16));
     }
 }
 
@@ -313,7 +317,8 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
 template <int EPI, typename OutT>
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ partial, int S, int M, int64_t npc,
-                     OutT* __restrict__ out, int64_t ldo, int64_t ncols_out, int col_blocks)
+                     OutT* __restrict__ out, int64_t ldo, int64_t ncols_out, int col_blocks,
+                     const OutT* __restrict__ resid, int64_t ldr, const OutT* __restrict__ bias)
 {
     const int row = blockIdx.x / col_blocks;
     const int64_t col = (int64_t)(blockIdx.x % col_blocks) * 256 + threadIdx.x;
@@ -332,7 +337,7 @@ splitk_reduce_kernel(const float* __restrict__ partial, int S, int M, int64_t np
         float v = 0.f;
         for (int s = 0; s < S; ++s)
             v += partial[((int64_t)s * M + row) * npc + col];
-        store_out(out + (int64_t)row * ldo + col, v);
+        store_out(out + (int64_t)row * ldo + col, plain_tail(v, resid, ldr, bias, row, col));
     }
 }
 
@@ -392,7 +397,8 @@ static void go_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipS
         W8 ? (const float*)((const uint8_t*)g.w + g.geom.scale_offset()) : nullptr;
     skinny_bf16_kernel<MT, U, NPB, EPI, SPLIT, OutT, W8><<<grid, dim3(SK_THREADS), 0, s>>>(
         (const uint16_t*)g.a, g.lda, g.geom.K, (const i32x4*)g.w, g.geom.nkc, p.chunks_per_split,
-        (OutT*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M, scales);
+        (OutT*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M, scales,
+        (const OutT*)g.resid, g.ldr, (const OutT*)g.bias);
 }
 
 template <int MT, int U, int NPB, int EPI, bool W8>
@@ -433,7 +439,8 @@ static void go_f32(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipSt
     dim3 grid((unsigned)p.grid_pb, (unsigned)p.splits, (unsigned)p.row_groups);
     skinny_f32_kernel<RT, U, EPI, SPLIT, float><<<grid, dim3(SK_THREADS), 0, s>>>(
         (const float*)g.a, g.lda, g.geom.K, (const f32x4*)g.w, g.geom.nkc, p.chunks_per_split,
-        (float*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M);
+        (float*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M,
+        (const float*)g.resid, g.ldr, (const float*)g.bias);
 }
 
 template <int RT, int EPI>
@@ -462,7 +469,7 @@ static void go_reduce(const GemmArgs& g, const SkinnyPlan& p, const float* parti
     const int col_blocks = (int)ceil_div(g.ncols_out, 256);
     splitk_reduce_kernel<EPI, OutT><<<dim3((unsigned)(col_blocks * g.M)), dim3(256), 0, s>>>(
         partial, p.splits, (int)g.M, g.geom.npb * 32, (OutT*)g.out, g.ldo, g.ncols_out,
-        col_blocks);
+        col_blocks, (const OutT*)g.resid, g.ldr, (const OutT*)g.bias);
 }
 
 hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)

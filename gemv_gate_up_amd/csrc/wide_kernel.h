@@ -116,7 +116,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1)
 wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, int M,
                  const uint16_t* __restrict__ w, int64_t nkc, int64_t npb,
                  uint16_t* __restrict__ out, int64_t ldo, int64_t ncols_out,
-                 int tiles_m, int tiles_n, int group_m)
+                 int tiles_m, int tiles_n, int group_m,
+                 const uint16_t* __restrict__ resid, int64_t ldr, const uint16_t* __restrict__ bias)
 {
     using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
     constexpr int FM = S::FM, FN = S::FN, PPW = S::PPW, APW = S::APW, NW = S::NW;
@@ -372,8 +373,17 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
                             ep[r * LROW + wn * WOW + jp * 16 + c] = f32_to_bf16(v);
                         } else {
                             const int cc = wn * WOW + jp * 32 + c;
-                            ep[r * LROW + cc] = f32_to_bf16(acc[fm][2 * jp][i]);
-                            ep[r * LROW + cc + 16] = f32_to_bf16(acc[fm][2 * jp + 1][i]);
+                            float v0 = acc[fm][2 * jp][i], v1 = acc[fm][2 * jp + 1][i];
+                            // bias and residual only inside the output
+                            const int64_t grow = m0 + pass * S::WTM + r, gcol = col0 + cc;
+                            if ((resid || bias) && grow < M) {
+                                if (gcol < ncols_out)
+                                    v0 = plain_tail(v0, resid, ldr, bias, grow, gcol);
+                                if (gcol + 16 < ncols_out)
+                                    v1 = plain_tail(v1, resid, ldr, bias, grow, gcol + 16);
+                            }
+                            ep[r * LROW + cc] = f32_to_bf16(v0);
+                            ep[r * LROW + cc + 16] = f32_to_bf16(v1);
                         }
                     }
                 }
@@ -424,7 +434,8 @@ static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m
     wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED>
         <<<dim3((unsigned)(tiles_m * tiles_n)), dim3(S::THREADS), S::LDS_BYTES, s>>>(
             (const uint16_t*)g.a, g.lda, g.geom.K, (int)g.M, (const uint16_t*)g.w, g.geom.nkc,
-            g.geom.npb, (uint16_t*)g.out, g.ldo, g.ncols_out, tiles_m, tiles_n, group_m);
+            g.geom.npb, (uint16_t*)g.out, g.ldo, g.ncols_out, tiles_m, tiles_n, group_m,
+            (const uint16_t*)g.resid, g.ldr, (const uint16_t*)g.bias);
     return hipGetLastError();
 }
 

@@ -180,6 +180,46 @@ int mlp_forward_ex(const void *x, const void *Wpacked, const void *Wdpacked, voi
                    void *workspace, size_t workspace_bytes, hipStream_t stream, int path);
 
 /*
+ * The MLP half of a pre-normalised transformer layer in one call:
+ *
+ *     n   = rmsnorm(r) = r / sqrt(mean(r^2) + eps) * gamma      (per row)
+ *     out = r + (silu(n . Wgate) (.) (n . Wup)) . Wdown (+ bias)
+ *
+ * "Anatomie d'un transformeur sur GPU", §1.1 layer skeleton (RMSNorm, the
+ * SwiGLU MLP, then the residual add) and §1.6 (its kernels 7 to 11, five
+ * launches in a classic implementation); the optional bias is the product
+ * plus bias of the "Affine" operation of "Où part le temps d'un token"
+ * (section "Deux opérations de trop"), added in the epilogue that finishes
+ * the down product.  The pages do not write RMSNorm out: this is the usual
+ * RMS form with a per-feature gain and a caller-given eps >= 0.
+ *
+ * r (M x d), gamma (d), bias (d, or NULL) and out (M x d) are device
+ * arrays in the activation type of dtype (bf16 for SWIGLU_BF16 and
+ * SWIGLU_BF16_FP8W, fp32 for SWIGLU_F32); Wpacked and Wdpacked as for
+ * mlp_forward.  n is rounded once to the activation type; the products
+ * accumulate in fp32; bias and residual are added in fp32 before the one
+ * rounding of out.  out may equal r (the residual stream updated in place);
+ * otherwise it must not overlap any input.  The workspace (device,
+ * mlp_block_workspace_bytes[_ex] bytes) holds n, h and any split-K
+ * partials.  r, gamma, out and the workspace must be 16-byte aligned, bias
+ * element-aligned.  Errors as for mlp_forward; eps negative, infinite or
+ * NaN is SWIGLU_ERR_INVALID_ARG.  The _ex variant forces the path of both
+ * products as mlp_forward_ex does.
+ */
+size_t mlp_block_workspace_bytes(int64_t M, int64_t d, int64_t dff, int dtype);
+size_t mlp_block_workspace_bytes_ex(int64_t M, int64_t d, int64_t dff, int dtype, int path);
+
+int mlp_block_forward(const void *r, const void *gamma, float eps, const void *Wpacked,
+                      const void *Wdpacked, const void *bias, void *out,
+                      int64_t M, int64_t d, int64_t dff, int dtype,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+int mlp_block_forward_ex(const void *r, const void *gamma, float eps, const void *Wpacked,
+                         const void *Wdpacked, const void *bias, void *out,
+                         int64_t M, int64_t d, int64_t dff, int dtype,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream, int path);
+
+/*
  * Recorded calls (HIP graphs).  A per-kernel fixed cost (launch, ramp-up,
  * drain) dominates short calls; replaying a recorded sequence of launches
  * from one host call is one of the two remedies that "Où part le temps d'un

@@ -163,3 +163,24 @@ def test_fp8_weight_sizes_and_paths():
         sw.SWIGLU_ERR_UNSUPPORTED
     # the down product's h is bf16 in the workspace, like the bf16 dtype
     assert sw.swiglu_workspace_bytes(16, 8192, 29568, W8, 1) >= 16 * 29568 * 2
+
+
+def test_mlp_block_arguments_and_workspace():
+    M, d, dff = 4, 64, 64
+    need = sw.mlp_block_workspace_bytes(M, d, dff, BF16)
+    # the normalised rows come first, then the MLP's own workspace
+    assert need == 256 * -(-(M * d * 2) // 256) + sw.swiglu_workspace_bytes(M, d, dff, BF16, 1)
+    blk = lambda *a, **k: sw.mlp_block_forward(*a, stream=0, **k)
+    assert blk(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, 0, d, dff, BF16) == sw.SWIGLU_OK
+    assert blk(FAKE, FAKE, -1.0, FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE,
+               need) == sw.SWIGLU_ERR_INVALID_ARG
+    assert blk(FAKE, FAKE, float("nan"), FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE,
+               need) == sw.SWIGLU_ERR_INVALID_ARG
+    assert blk(FAKE, None, 1e-5, FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE,
+               need) == sw.SWIGLU_ERR_INVALID_ARG
+    assert blk(FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE + 1, FAKE, M, d, dff, BF16, FAKE,
+               need) == sw.SWIGLU_ERR_MISALIGNED
+    assert blk(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE,
+               need - 256) == sw.SWIGLU_ERR_WORKSPACE
+    assert sw.mlp_block_forward_ex(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, M, d, dff, F32, FAKE,
+                                   need, 0, sw.SWIGLU_PATH_WIDE) == sw.SWIGLU_ERR_UNSUPPORTED
