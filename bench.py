@@ -70,7 +70,8 @@ def traffic_from_profile(workload: str, kernel: str):
 class Runner:
     """Device buffers and the C-ABI call for one workload."""
 
-    def __init__(self, w: wl.Workload, copies: int, path: int = 0, graph: bool = False):
+    def __init__(self, w: wl.Workload, copies: int, path: int = 0, graph: bool = False,
+                 block: bool = False):
         import torch
         import gemv_gate_up_amd as sw
         self.torch, self.sw, self.w = torch, sw, w
@@ -100,7 +101,17 @@ class Runner:
         ncols = w.d if w.with_down else w.dff
         self.out = torch.empty((w.M, ncols), dtype=tdt, device="cuda")
         self.req_path = path
-        self.ws_bytes = sw.swiglu_workspace_bytes_ex(w.M, w.d, w.dff, w.dtype, int(w.with_down), path)
+        self.block = block
+        if block:
+            # the MLP half of a layer: x doubles as the residual stream r;
+            # gain and bias drawn like the activations (seeded)
+            assert w.with_down, "the block needs the down projection"
+            self.gamma = dev(wl.to_storage(1.0 + 0.1 * wl.normal(90, (w.d,), 1.0), w.dtype))
+            self.bias = dev(wl.to_storage(wl.normal(91, (w.d,), 0.1), w.dtype))
+            self.ws_bytes = sw.mlp_block_workspace_bytes_ex(w.M, w.d, w.dff, w.dtype, path)
+        else:
+            self.ws_bytes = sw.swiglu_workspace_bytes_ex(w.M, w.d, w.dff, w.dtype,
+                                                         int(w.with_down), path)
         if self.ws_bytes < 0:
             raise RuntimeError("path %d: %s" % (path, sw.swiglu_status_string(self.ws_bytes)))
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
@@ -134,7 +145,12 @@ class Runner:
     def step(self, i: int) -> None:
         w, sw = self.w, self.sw
         xp, wpp, wdpp = self.args[i % self.copies]
-        if self.graphs:
+        if self.block:
+            rc = sw._lib.mlp_block_forward_ex(xp, self.gamma.data_ptr(), 1e-6, wpp, wdpp,
+                                              self.bias.data_ptr(), self.out.data_ptr(), w.M, w.d,
+                                              w.dff, w.dtype, self.ws.data_ptr(), self.ws_bytes,
+                                              self.sh, self.req_path)
+        elif self.graphs:
             rc = sw._lib.swiglu_graph_launch(self.graphs[i % self.copies], self.sh)
         elif self.req_path and w.with_down:
             rc = sw._lib.mlp_forward_ex(xp, wpp, wdpp, self.out.data_ptr(), w.M, w.d, w.dff,
@@ -183,9 +199,15 @@ def dominant_kernel(w: wl.Workload, path: int) -> str:
     return "skinny_f32_kernel" if w.dtype == wl.F32 else "skinny_bf16_kernel"
 
 
+def block_bytes(w: wl.Workload) -> int:
+    """Algorithmic bytes of the MLP block: the MLP's, plus gamma and bias
+    (r is the MLP's x, out its y)."""
+    return w.algorithmic_bytes() + 2 * w.d * w.elem_bytes
+
+
 def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0,
-            graph: bool = False) -> dict:
-    r = Runner(w, copies, path, graph)
+            graph: bool = False, block: bool = False) -> dict:
+    r = Runner(w, copies, path, graph, block)
     t = r.time(steps, warmup)
     kern = dominant_kernel(w, r.path)
     per_launch_ms = t["event_ms_per_launch"]
@@ -193,7 +215,7 @@ def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0,
         r.path in (2, 3) or r.sw.swiglu_workspace_bytes(w.M, w.d, w.dff, w.dtype, 0) == 0)
     res = {"runner": r, "timing": t, "kernel": kern, "path": r.path,
            "single_kernel_step": single_kernel}
-    bytes_alg = w.algorithmic_bytes()
+    bytes_alg = block_bytes(w) if block else w.algorithmic_bytes()
     flops_alg = w.algorithmic_flops()
     hbm_bound = flops_alg / bytes_alg < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if hbm_bound:
@@ -206,7 +228,8 @@ def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0,
                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
     # recorded counters are for the dispatcher's own path
-    res["roofline"]["traffic"] = traffic_from_profile(w.name, kern) if not path else None
+    res["roofline"]["traffic"] = (traffic_from_profile(w.name, kern)
+                                  if not (path or graph or block) else None)
     res["roofline"]["kernel"] = kern
     res["roofline"]["kernel_ms"] = round(per_launch_ms, 5)
     return res
@@ -276,6 +299,9 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--block", action="store_true",
+                    help="time the MLP block (RMSNorm, MLP, bias and residual) on a workload "
+                         "with the down projection")
     ap.add_argument("--graph", action="store_true",
                     help="replay recorded calls (HIP graphs) instead of direct calls")
     ap.add_argument("--path", default="auto", choices=sorted(PATHS),
@@ -300,9 +326,10 @@ def main() -> int:
     one_copy = 2 * w.d * w.dff * w.weight_bytes
     copies = max(1, -(-(1 << 30) // one_copy)) if one_copy < (1 << 30) else 1
     log("workload %s: %s, %d weight copies" % (w.name, w, copies))
-    m = measure(w, args.steps, args.warmup, copies, PATHS[args.path], args.graph)
+    m = measure(w, args.steps, args.warmup, copies, PATHS[args.path], args.graph, args.block)
     t = m["timing"]
-    value_bytes = w.algorithmic_bytes() / (t["wall_ms_per_step"] * 1e-3) / 1e9
+    alg_bytes = block_bytes(w) if args.block else w.algorithmic_bytes()
+    value_bytes = alg_bytes / (t["wall_ms_per_step"] * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": round(value_bytes, 1),
@@ -318,8 +345,8 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights, bf16 RNE)",
         "config": {"workload": w.name, "M": w.M, "d": w.d, "dff": w.dff,
                    "with_down": w.with_down, "path": PATH_NAMES[m["path"]],
-                   "weight_copies": copies, "graph": bool(args.graph),
-                   "algorithmic_bytes": w.algorithmic_bytes(),
+                   "weight_copies": copies, "graph": bool(args.graph), "block": bool(args.block),
+                   "algorithmic_bytes": alg_bytes,
                    "algorithmic_flops": w.algorithmic_flops()},
         "roofline": m["roofline"],
         "timing_ms": {k: round(v, 5) for k, v in t.items()},

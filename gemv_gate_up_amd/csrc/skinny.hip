@@ -367,9 +367,14 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
     p.row_groups = ceil_div(g.M, p.row_tile);
     // Split K only when there are too few pair blocks (units of weight
     // streaming) to keep every CU busy; two pair blocks per workgroup are
-    // still two units of work.
+    // still two units of work.  A gate/up product over more than 16 rows
+    // carries several row tiles of matrix work per pair block and its
+    // partials grow with M: one pair block per CU is enough there (the
+    // 0.5B-class MLP at 64 rows: 14.1 us with a 2-way split and its second
+    // pass, 11.1 us without).
     const int64_t base = p.grid_pb * p.row_groups;
-    const int64_t target = 2 * (int64_t)num_cus;
+    const int64_t target =
+        (g.epi == EPI_SWIGLU && p.row_tile > 16) ? (int64_t)num_cus : 2 * (int64_t)num_cus;
     const int64_t min_chunks = 8;
     int64_t S = 1;
     while (base * S < target && g.geom.nkc / (2 * S) >= min_chunks && S < 64)
