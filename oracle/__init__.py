@@ -69,6 +69,16 @@ def _bind(lib):
     lib.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
     lib.oracle_quantize_e4m3_columns.restype = ctypes.c_int
     lib.oracle_quantize_e4m3_columns.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_e2m1_to_double.restype = ctypes.c_double
+    lib.oracle_e2m1_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_from_double.restype = ctypes.c_uint8
+    lib.oracle_e2m1_from_double.argtypes = [ctypes.c_double]
+    lib.oracle_mx_shared_exponent.restype = ctypes.c_int
+    lib.oracle_mx_shared_exponent.argtypes = [ctypes.c_double]
+    lib.oracle_quantize_mxfp4_columns.restype = ctypes.c_int
+    lib.oracle_quantize_mxfp4_columns.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_dequantize_mxfp4_columns.restype = ctypes.c_int
+    lib.oracle_dequantize_mxfp4_columns.argtypes = [vp, vp, i64, i64, dp]
     lib.oracle_rmsnorm_rows.restype = ctypes.c_int
     lib.oracle_rmsnorm_rows.argtypes = [ctypes.c_int, vp, vp, ctypes.c_double, i64, i64, dp]
     lib.oracle_dequantize_e4m3_columns.restype = ctypes.c_int
@@ -199,6 +209,44 @@ def dequantize_e4m3(codes, scales, lib=None) -> np.ndarray:
     if (lib or _load()).oracle_dequantize_e4m3_columns(_ptr(codes), _ptr(scales), K, N,
                                                        _ptr(out)):
         raise ValueError("oracle_dequantize_e4m3_columns failed")
+    return out
+
+
+def e2m1_to_double(code: int, lib=None) -> float:
+    return (lib or _load()).oracle_e2m1_to_double(int(code))
+
+
+def e2m1_from_double(v: float, lib=None) -> int:
+    """Nearest E2M1 code (ties to even, saturating at 6)."""
+    return (lib or _load()).oracle_e2m1_from_double(float(v))
+
+
+def mx_shared_exponent(amax: float, lib=None) -> int:
+    return (lib or _load()).oracle_mx_shared_exponent(float(amax))
+
+
+def quantize_mxfp4(w, lib=None):
+    """MXFP4 quantisation of a K x N bf16 matrix along K: returns (codes
+    uint8 K x N, one E2M1 code each; scales uint8 ceil(K/32) x N, E8M0)."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    K, N = w.shape
+    codes = np.empty((K, N), dtype=np.uint8)
+    scales = np.empty(((K + 31) // 32, N), dtype=np.uint8)
+    if (lib or _load()).oracle_quantize_mxfp4_columns(_ptr(w), K, N, _ptr(codes), _ptr(scales)):
+        raise ValueError("oracle_quantize_mxfp4_columns failed")
+    return codes, scales
+
+
+def dequantize_mxfp4(codes, scales, lib=None) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    K, N = codes.shape
+    if scales.shape != ((K + 31) // 32, N):
+        raise ValueError("one scale per 32-row block and column")
+    out = np.empty((K, N), dtype=np.float64)
+    if (lib or _load()).oracle_dequantize_mxfp4_columns(_ptr(codes), _ptr(scales), K, N,
+                                                        _ptr(out)):
+        raise ValueError("oracle_dequantize_mxfp4_columns failed")
     return out
 
 

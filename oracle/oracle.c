@@ -151,6 +151,102 @@ int oracle_quantize_e4m3_columns(const uint16_t *w, int64_t K, int64_t N, uint8_
     return 0;
 }
 
+/*
+ * MXFP4 weights (OCP Microscaling v1.0, MXFP4): blocks of 32 consecutive K
+ * values of one column share a power-of-two scale X = 2^s (an E8M0 code
+ * s + 127); each value is stored as an E2M1 code of w / X.  The shared
+ * exponent is s = floor(log2(amax)) - 2, amax the block's largest
+ * magnitude and 2 the exponent of E2M1's largest power of two (4), so
+ * amax / X lies in [4, 8); s is clamped to [-126, 127] so that every scale
+ * is a normal fp32 number, and an all-zero block takes s = 0.  w / X is
+ * exact; the element code is the nearest E2M1 value, ties to the even code,
+ * saturating at +-6.
+ *
+ * E2M1: sign bit 3, exponent bits 2-1 with bias 1, mantissa bit 0; exponent
+ * 0 holds the subnormal 0.5 * m, otherwise (1 + m/2) * 2^(e-1): the values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ */
+double oracle_e2m1_to_double(uint8_t code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* Nearest E2M1 code (ties to the even code, saturating at 6); within a
+ * binade [2^b, 2^(b+1)) the values are spaced 2^(b-1), below 1 by 0.5. */
+uint8_t oracle_e2m1_from_double(double v)
+{
+    uint8_t sign = signbit(v) ? 0x8 : 0x0;
+    double a = fabs(v);
+    if (a >= 6.0)
+        return sign | 0x7;
+    int e;
+    frexp(a, &e);
+    int b = e - 1;
+    double step = (a == 0.0 || b < 0) ? 0.5 : ldexp(1.0, b - 1);
+    double r = nearbyint(a / step) * step;
+    if (r < 1.0)
+        return sign | (uint8_t)(r / 0.5);
+    frexp(r, &e);
+    b = e - 1;
+    int m = (int)(r / ldexp(1.0, b - 1)) - 2;
+    return sign | (uint8_t)(((b + 1) << 1) | m);
+}
+
+/* Shared exponent of a block with largest magnitude amax (see above). */
+int oracle_mx_shared_exponent(double amax)
+{
+    if (amax == 0.0)
+        return 0;
+    int e;
+    frexp(amax, &e);
+    int s = (e - 1) - 2;
+    return s < -126 ? -126 : (s > 127 ? 127 : s);
+}
+
+/*
+ * Quantises the K x N row-major bf16 matrix w to MXFP4 along K: codes
+ * (K x N, one E2M1 code per byte) and E8M0 scale codes (ceil(K/32) x N,
+ * block b covering rows 32b .. 32b+31).
+ */
+int oracle_quantize_mxfp4_columns(const uint16_t *w, int64_t K, int64_t N, uint8_t *codes,
+                                  uint8_t *scales)
+{
+    if (K <= 0 || N <= 0 || !w || !codes || !scales)
+        return -1;
+    int64_t nb = (K + 31) / 32;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < nb; ++b) {
+            int64_t k1 = 32 * b + 32 < K ? 32 * b + 32 : K;
+            double amax = 0.0;
+            for (int64_t k = 32 * b; k < k1; ++k) {
+                double a = fabs(oracle_bf16_to_double(w[k * N + n]));
+                if (a > amax)
+                    amax = a;
+            }
+            int s = oracle_mx_shared_exponent(amax);
+            scales[b * N + n] = (uint8_t)(s + 127);
+            for (int64_t k = 32 * b; k < k1; ++k)
+                codes[k * N + n] = oracle_e2m1_from_double(ldexp(oracle_bf16_to_double(w[k * N + n]), -s));
+        }
+    }
+    return 0;
+}
+
+/* out[k][n] = 2^(scale[k/32][n] - 127) * e2m1(code[k][n]), exact in fp64. */
+int oracle_dequantize_mxfp4_columns(const uint8_t *codes, const uint8_t *scales, int64_t K,
+                                    int64_t N, double *out)
+{
+    if (K <= 0 || N <= 0 || !codes || !scales || !out)
+        return -1;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            out[k * N + n] = ldexp(oracle_e2m1_to_double(codes[k * N + n]),
+                                   (int)scales[(k / 32) * N + n] - 127);
+    return 0;
+}
+
 /* out[k][n] = scale[n] * e4m3(code[k][n]), exact in fp64. */
 int oracle_dequantize_e4m3_columns(const uint8_t *codes, const float *scales, int64_t K,
                                    int64_t N, double *out)

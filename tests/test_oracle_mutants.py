@@ -43,6 +43,15 @@ MUTANTS = {
                             "out[k * N + n] = oracle_e4m3_to_double"),
     "f64_read_as_f32": ("return ((const double *)p)[i];",
                         "return (double)((const float *)p)[i];"),
+    # MXFP4
+    "e2m1_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e - 2)"),
+    "e2m1_ties_away": ("nearbyint(a / step) * step", "round(a / step) * step"),
+    "mx_exponent_offset": ("int s = (e - 1) - 2;", "int s = (e - 1) - 3;"),
+    "mx_zero_block": ("    if (amax == 0.0)\n        return 0;\n    int e;",
+                      "    if (amax == 0.0)\n        return -126;\n    int e;"),
+    "mx_unscaled_codes": ("oracle_e2m1_from_double(ldexp(oracle_bf16_to_double(w[k * N + n]), -s))",
+                          "oracle_e2m1_from_double(oracle_bf16_to_double(w[k * N + n]))"),
+    "mx_first_block_scale": ("(int)scales[(k / 32) * N + n] - 127", "(int)scales[n] - 127"),
     # RMSNorm
     "rms_no_eps": ("sqrt(ss / (double)d + eps)", "sqrt(ss / (double)d)"),
     "rms_sum_not_mean": ("sqrt(ss / (double)d + eps)", "sqrt(ss + eps)"),
@@ -94,6 +103,22 @@ def pin_failures(lib):
                               oracle.swiglu(inp["x"], inp["wg"], inp["wu"], lib=lib))
 
     check("f64_path", f64_path)
+    # MXFP4: E2M1 values, ties, the shared exponent, a two-block exact grid
+    check("e2m1", lambda: [oracle.e2m1_to_double(c, lib=lib) for c in (1, 5, 7)] == [0.5, 3.0, 6.0]
+          and [oracle.e2m1_from_double(v, lib=lib) for v in (0.75, 2.5, 5.0)] == [2, 4, 6])
+    check("mx_exp", lambda: [oracle.mx_shared_exponent(a, lib=lib) for a in (1.0, 6.0, 0.0)]
+          == [-2, 0, 0])
+
+    def mx_grid():
+        col = np.array([6.0, -0.5, 1.5] + [0.0] * 29 + [4.0, 3.0, -1.0], dtype=np.float32)
+        col[:32] *= np.float32(2.0 ** -3)
+        col[32:] *= np.float32(2.0 ** 2)
+        q, sc = oracle.quantize_mxfp4(wl.f32_to_bf16_bits(col.reshape(-1, 1)), lib=lib)
+        deq = oracle.dequantize_mxfp4(q, sc, lib=lib)[:, 0]
+        return (list(sc[:, 0]) == [124, 129] and list(q[[0, 1, 2, 32, 33, 34], 0]) == [7, 9, 3, 6, 5, 10]
+                and np.array_equal(deq, col.astype(np.float64)))
+
+    check("mx_grid", mx_grid)
     # RMSNorm: the hand-worked row [3, 4] (n = [0.6, 0.8] * sqrt 2), a gain,
     # and the eps closed form at d = 1
     check("rmsnorm_hand", lambda: np.allclose(
