@@ -243,9 +243,17 @@ def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float) -> dict:
     x = inp["x"][:w.M]
     if w.dtype == wl.FP8W:   # quantised once, outside the timing
         q = {k: oracle.quantize_e4m3(inp[k]) for k in ("wg", "wu", "wd") if k in inp}
+    if w.dtype == wl.MXFP4W:
+        q = {k: oracle.dequantize_mxfp4(*oracle.quantize_mxfp4(inp[k]))
+             for k in ("wg", "wu", "wd") if k in inp}
+        x = oracle.to_double(x)
     reps, t0 = 0, time.perf_counter()
     while True:
-        if w.dtype == wl.FP8W and w.with_down:
+        if w.dtype == wl.MXFP4W and w.with_down:
+            oracle.mlp(x, q["wg"], q["wu"], q["wd"], nthreads=threads)
+        elif w.dtype == wl.MXFP4W:
+            oracle.swiglu(x, q["wg"], q["wu"], nthreads=threads)
+        elif w.dtype == wl.FP8W and w.with_down:
             oracle.mlp_fp8w(x, *q["wg"], *q["wu"], *q["wd"], nthreads=threads)
         elif w.dtype == wl.FP8W:
             oracle.swiglu_fp8w(x, *q["wg"], *q["wu"], nthreads=threads)
@@ -323,7 +331,7 @@ def main() -> int:
     if args.probe:
         return probe()
     w = wl.WORKLOADS[args.workload]
-    one_copy = 2 * w.d * w.dff * w.weight_bytes
+    one_copy = int(2 * w.d * w.dff * w.weight_bytes)
     copies = max(1, -(-(1 << 30) // one_copy)) if one_copy < (1 << 30) else 1
     log("workload %s: %s, %d weight copies" % (w.name, w, copies))
     m = measure(w, args.steps, args.warmup, copies, PATHS[args.path], args.graph, args.block)

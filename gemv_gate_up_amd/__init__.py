@@ -23,6 +23,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "swiglu.h")
 SWIGLU_F32 = 0
 SWIGLU_BF16 = 1
 SWIGLU_BF16_FP8W = 2
+SWIGLU_BF16_MXFP4W = 3
 
 SWIGLU_OK = 0
 SWIGLU_ERR_INVALID_ARG = -1

@@ -35,7 +35,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_sizes(int64_t M, int64_t d, int64_t dff, int dtype)
 {
-    if (dtype != SWIGLU_F32 && dtype != SWIGLU_BF16 && dtype != SWIGLU_BF16_FP8W)
+    if (dtype != SWIGLU_F32 && dtype != SWIGLU_BF16 && dtype != SWIGLU_BF16_FP8W &&
+        dtype != SWIGLU_BF16_MXFP4W)
         return SWIGLU_ERR_UNSUPPORTED;
     if (M < 0 || d <= 0 || dff <= 0)
         return SWIGLU_ERR_INVALID_ARG;

@@ -31,12 +31,22 @@
 // and widens into the B operands of two bf16 MFMAs.  K is padded to 64.
 // After the pieces comes one fp32 scale per packed column, ordered
 // [pair block][half][16] (entry 32p + 16h + c), zero for padded columns.
+//
+// MXFP4 weights (DT_MXFP4W: OCP MX E2M1 codes with one E8M0 scale per 32
+// consecutive K values of a column): a lane's 16 bytes hold, for each of
+// four consecutive 32-K chunks j, the 8 values of its k-group (byte 4j + i
+// holds k0 + 32j + 8g + 2i in its low nibble and the next K value in its
+// high nibble), so one piece covers 16 columns by 128 K and widens into the
+// B operands of four MFMAs; each chunk of a column is exactly one MX block.
+// K is padded to 128.  After the pieces come the block scales, 64 bytes per
+// piece ordered [pair block][k piece][half][column c][chunk j], so that lane
+// l reads the four scales of its column as one dword.
 #pragma once
 #include <stdint.h>
 
 namespace swg {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8W = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8W = 2, DT_MXFP4W = 3 };
 enum : int { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 
 constexpr int PIECE_BYTES = 1024;
@@ -49,10 +59,10 @@ __host__ __device__ constexpr inline int elem_bytes(int dt) { return dt == DT_F3
 __host__ __device__ constexpr inline int act_vec_elems(int dt) { return dt == DT_F32 ? 4 : 8; }
 // K covered by one piece, and the K padding.
 __host__ __device__ constexpr inline int chunk_k(int dt) {
-    return dt == DT_F32 ? 16 : (dt == DT_BF16 ? 32 : 64);
+    return dt == DT_F32 ? 16 : (dt == DT_BF16 ? 32 : (dt == DT_FP8W ? 64 : 128));
 }
 __host__ __device__ constexpr inline int k_align(int dt) {
-    return dt == DT_FP8W ? 64 : 2 * chunk_k(dt);
+    return dt == DT_FP8W || dt == DT_MXFP4W ? chunk_k(dt) : 2 * chunk_k(dt);
 }
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -69,10 +79,11 @@ struct PackGeom {
     int cols_per_pb;    // output columns per pair block (16 or 32)
     int dt;
     __host__ __device__ int64_t piece_bytes() const { return npb * nkc * 2 * PIECE_BYTES; }
-    // FP8 weights: the column scales follow the pieces
+    // FP8 and MXFP4 weights: the scales follow the pieces
     __host__ __device__ int64_t scale_offset() const { return piece_bytes(); }
     __host__ __device__ int64_t bytes() const {
-        return piece_bytes() + (dt == DT_FP8W ? npb * 32 * 4 : 0);
+        return piece_bytes() + (dt == DT_FP8W ? npb * 32 * 4 : 0) +
+               (dt == DT_MXFP4W ? npb * nkc * 2 * 64 : 0);
     }
     // output row width when the result is kept padded (workspace h)
     __host__ __device__ int64_t padded_cols() const { return npb * cols_per_pb; }

@@ -12,6 +12,8 @@
 // magnitude and stores scale = amax / 448, a second pass writes the codes of
 // w / scale.  Both divisions are IEEE fp32 (__fdiv_rn) and the encoding is
 // exact integer arithmetic, so the codes are fully determined by the input.
+// MXFP4 weights likewise: block scales first, then the codes of w / 2^s
+// (exact: a power-of-two scale).
 #include "device_common.h"
 #include "launch.h"
 
@@ -125,9 +127,100 @@ pack_fp8_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ 
     dst[v] = i32x4{(int)word[0], (int)word[1], (int)word[2], (int)word[3]};
 }
 
+// MXFP4: one thread per (pair block, k piece, half, column, chunk), in the
+// order of the scale table, so thread t writes byte t: the E8M0 code of the
+// block's shared exponent floor(log2 amax) - 2, clamped to [-126, 127]
+// (code 127, exponent 0, for an all-zero block).
+__global__ void __launch_bounds__(256)
+mx_scale_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1,
+                uint8_t* __restrict__ scales, int64_t K, int64_t N, int64_t nkc, int64_t total,
+                int plain)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= total)
+        return;
+    const int j = (int)(t % 4), c = (int)((t / 4) % 16), h = (int)((t / 64) % 2);
+    const int64_t kc = (t / 128) % nkc, pb = t / (128 * nkc);
+    const int64_t n = packed_col(pb, h, c, plain);
+    const uint16_t* src = (plain || h == 0) ? src0 : src1;
+    const int64_t k0 = kc * 128 + j * 32;
+    float amax = 0.f;
+    if (n < N)
+        for (int64_t k = k0; k < k0 + 32 && k < K; ++k)
+            amax = fmaxf(amax, fabsf(bf16_to_f32(src[k * N + n])));
+    int s = 0;
+    if (amax > 0.f) {
+        int e;
+        frexpf(amax, &e);             // amax = f * 2^e, f in [0.5, 1)
+        s = e - 1 - 2;
+        s = s < -126 ? -126 : (s > 127 ? 127 : s);
+    }
+    scales[t] = (uint8_t)(s + 127);
+}
+
+// E2M1 code of q: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the
+// even code (the thresholds below are the midpoints; a tie lands on the
+// side whose code is even), saturating at 6; the sign goes to bit 3.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+    const uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 28) & 8u;
+    const float a = fabsf(q);
+    uint32_t c;
+    if (a <= 0.25f)      c = 0;
+    else if (a < 0.75f)  c = 1;
+    else if (a <= 1.25f) c = 2;
+    else if (a < 1.75f)  c = 3;
+    else if (a <= 2.5f)  c = 4;
+    else if (a < 3.5f)   c = 5;
+    else if (a <= 5.0f)  c = 6;
+    else                 c = 7;
+    return sign | c;
+}
+
+// One thread per 16-byte vector of the MXFP4 pieces.
+__global__ void __launch_bounds__(256)
+pack_mxfp4_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1,
+                  const uint8_t* __restrict__ scales, i32x4* __restrict__ dst, int64_t K,
+                  int64_t N, int64_t nkc, int64_t total_vecs, int plain)
+{
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= total_vecs)
+        return;
+    const int lane = (int)(v % PIECE_VECS);
+    const int64_t piece = v / PIECE_VECS;       // ((pb * nkc + kc) * 2 + h)
+    const int h = (int)(piece % 2);
+    const int64_t kc = (piece / 2) % nkc;
+    const int64_t pb = piece / (2 * nkc);
+    const int c = lane % 16, g = lane / 16;
+    const int64_t n = packed_col(pb, h, c, plain);
+    const uint16_t* src = (plain || h == 0) ? src0 : src1;
+    uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int s = (int)scales[piece * 64 + c * 4 + j] - 127;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = kc * 128 + j * 32 + g * 8 + e;
+            const float w = (k < K && n < N) ? bf16_to_f32(src[k * N + n]) : 0.f;
+            word[j] |= e2m1_code(ldexpf(w, -s)) << (4 * e);
+        }
+    }
+    dst[v] = i32x4{(int)word[0], (int)word[1], (int)word[2], (int)word[3]};
+}
+
 hipError_t launch_pack(const void* src0, const void* src1, void* dst, const PackGeom& g,
                        int plain, hipStream_t s)
 {
+    if (g.dt == DT_MXFP4W) {
+        uint8_t* scales = (uint8_t*)dst + g.scale_offset();
+        const int64_t nsc = g.npb * g.nkc * 2 * 64;
+        mx_scale_kernel<<<dim3((unsigned)ceil_div(nsc, 256)), dim3(256), 0, s>>>(
+            (const uint16_t*)src0, (const uint16_t*)src1, scales, g.K, g.N, g.nkc, nsc, plain);
+        const int64_t total = g.npb * g.nkc * 2 * PIECE_VECS;
+        pack_mxfp4_kernel<<<dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s>>>(
+            (const uint16_t*)src0, (const uint16_t*)src1, scales, (i32x4*)dst, g.K, g.N, g.nkc,
+            total, plain);
+        return hipGetLastError();
+    }
     if (g.dt == DT_FP8W) {
         float* scales = (float*)((uint8_t*)dst + g.scale_offset());
         const int64_t slots = g.npb * 32;

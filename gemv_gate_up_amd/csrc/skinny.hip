@@ -20,10 +20,13 @@
 // throughput, and above M = 4 plain fp32 FMA on the VALU would take longer
 // than streaming the weights.  fp32 weights use VALU FMA.
 //
-// FP8 weights (W8) halve the streamed bytes: each 16-byte load brings 16
-// E4M3 codes that widen exactly to bf16 (every E4M3 value is a bf16 value)
-// with gfx950's packed conversion, feeding two MFMAs over two 32-K chunks;
-// the per-column scale multiplies the finished fp32 sum.
+// FP8 weights (WF = WF_FP8) halve the streamed bytes: each 16-byte load
+// brings 16 E4M3 codes that widen exactly to bf16 (every E4M3 value is a
+// bf16 value) with gfx950's packed conversion, feeding two MFMAs over two
+// 32-K chunks; the per-column scale multiplies the finished fp32 sum.
+// MXFP4 weights (WF_MXFP4) quarter them: 32 E2M1 codes per load feed four
+// MFMAs, one per 32-K chunk, and since each chunk of a column is one MX
+// block its power-of-two scale is applied by the same conversion (exact).
 #include "device_common.h"
 #include "launch.h"
 
@@ -31,6 +34,24 @@ namespace swg {
 
 constexpr int SK_WAVES = 4;
 constexpr int SK_THREADS = SK_WAVES * 64;
+
+constexpr int WF_BF16 = 0, WF_FP8 = 1, WF_MXFP4 = 2;
+
+// Eight E2M1 codes (one dword, low nibble first) times 2^s -> eight bf16
+// values in the same order; exact (sc = 2^s, a normal fp32 number).
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(int w, float sc) {
+    i32x4 r;
+    r.x = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+    r.y = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+    r.z = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+    r.w = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// E8M0 scale code (1..254 here) -> 2^(code - 127) as fp32.
+__device__ __forceinline__ float e8m0_scale(uint32_t code) {
+    return __builtin_bit_cast(float, code << 23);
+}
 
 // Eight E4M3 codes (two dwords, lowest byte first) -> eight bf16 values in
 // the same order; exact.
@@ -47,18 +68,20 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(int lo, int hi) {
 // Each wave covers NPB consecutive pair blocks, so one activation fragment
 // (MT 16-row tiles of x over a 32-K chunk) feeds 2*NPB*MT MFMAs; with 16 or
 // more rows, re-reading that fragment per pair block would cost half as many
-// bytes again as the weights.  With W8 a piece spans two chunks (CH = 2),
-// so each step loads two activation fragments per row tile.
-template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT, bool W8>
+// bytes again as the weights.  FP8 and MXFP4 pieces span two and four
+// chunks (CH), so each step loads CH activation fragments per row tile.
+template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT, int WF>
 __global__ void __launch_bounds__(SK_THREADS)
 skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                    const i32x4* __restrict__ w, int64_t nkc, int64_t cps,
                    OutT* __restrict__ out, int64_t ldo, int64_t ncols_out,
                    float* __restrict__ partial, int64_t npc, int M,
-                   const float* __restrict__ scales, const OutT* __restrict__ resid, int64_t ldr,
+                   const void* __restrict__ scales, const OutT* __restrict__ resid, int64_t ldr,
                    const OutT* __restrict__ bias)
 {
-    constexpr int CH = W8 ? 2 : 1;   // 32-K chunks per piece
+    constexpr bool W8 = WF == WF_FP8;
+    constexpr int CH = WF == WF_BF16 ? 1 : (WF == WF_FP8 ? 2 : 4);   // 32-K chunks per piece
+    const float* colscale = (const float*)scales;                       // FP8: per column
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t pb0 = (int64_t)blockIdx.x * NPB;
@@ -67,6 +90,9 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
     const int64_t kbeg = (int64_t)s * cps;
     const int64_t kend = kbeg + cps < nkc ? kbeg + cps : nkc;
     const i32x4* wp = w + pb0 * nkc * 2 * PIECE_VECS + lane;
+    // MXFP4: 16 dwords of block scales per piece; lane l reads its column's
+    const uint32_t* blkscale =
+        WF == WF_MXFP4 ? (const uint32_t*)scales + pb0 * nkc * 2 * 16 + (lane & 15) : nullptr;
 
     // A operand of lane l: row l % 16 of each 16-row tile, k-group l / 16.
     const int arow = lane & 15;
@@ -83,6 +109,7 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
 
     for (int64_t kb = kbeg + wave; kb < kend; kb += SK_WAVES * U) {
         i32x4 wg[NPB][U], wu[NPB][U];
+        uint32_t sgb[WF == WF_MXFP4 ? NPB : 1][U], sub[WF == WF_MXFP4 ? NPB : 1][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t kc = kb + SK_WAVES * u;
@@ -91,9 +118,17 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                 if (kc < kend) {
                     wg[p][u] = load_nt16(wp + (p * nkc * 2 + kc * 2) * PIECE_VECS);
                     wu[p][u] = load_nt16(wp + (p * nkc * 2 + kc * 2 + 1) * PIECE_VECS);
+                    if constexpr (WF == WF_MXFP4) {
+                        sgb[p][u] = blkscale[(p * nkc * 2 + kc * 2) * 16];
+                        sub[p][u] = blkscale[(p * nkc * 2 + kc * 2 + 1) * 16];
+                    }
                 } else {
                     wg[p][u] = i32x4{0, 0, 0, 0};
                     wu[p][u] = i32x4{0, 0, 0, 0};
+                    if constexpr (WF == WF_MXFP4) {
+                        sgb[p][u] = 127u * 0x01010101u;   // scale 1 for the zero padding
+                        sub[p][u] = 127u * 0x01010101u;
+                    }
                 }
             }
         }
@@ -121,7 +156,10 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
 #pragma unroll
                 for (int ch = 0; ch < CH; ++ch) {
                     bf16x8 bg, bu;
-                    if constexpr (W8) {
+                    if constexpr (WF == WF_MXFP4) {
+                        bg = e2m1x8_to_bf16(wg[p][u][ch], e8m0_scale((sgb[p][u] >> (8 * ch)) & 255u));
+                        bu = e2m1x8_to_bf16(wu[p][u][ch], e8m0_scale((sub[p][u] >> (8 * ch)) & 255u));
+                    } else if constexpr (W8) {
                         bg = ch == 0 ? e4m3x8_to_bf16(wg[p][u].x, wg[p][u].y)
                                      : e4m3x8_to_bf16(wg[p][u].z, wg[p][u].w);
                         bu = ch == 0 ? e4m3x8_to_bf16(wu[p][u].x, wu[p][u].y)
@@ -165,8 +203,8 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
         }
         __syncthreads();
         // column scales of the FP8 weights: entry 32 * pb + 16 * half + c
-        const float gs = W8 ? scales[pb * 32 + c] : 1.f;
-        const float us = W8 ? scales[pb * 32 + 16 + c] : 1.f;
+        const float gs = W8 ? colscale[pb * 32 + c] : 1.f;
+        const float us = W8 ? colscale[pb * 32 + 16 + c] : 1.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             float g = 0.f, u = 0.f;
@@ -391,50 +429,55 @@ size_t skinny_partial_bytes(const GemmArgs& g, const SkinnyPlan& p)
     return (size_t)p.splits * (size_t)g.M * (size_t)(g.geom.npb * 32) * sizeof(float);
 }
 
-template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT, bool W8>
+template <int MT, int U, int NPB, int EPI, bool SPLIT, typename OutT, int WF>
 static void go_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     // With two pair blocks per workgroup and an odd count, the last
     // workgroup's second pair block is padding (zero weights, never stored):
     // the packed buffer holds a multiple of 8 pair blocks.
     dim3 grid((unsigned)ceil_div(p.grid_pb, NPB), (unsigned)p.splits, (unsigned)p.row_groups);
-    const float* scales =
-        W8 ? (const float*)((const uint8_t*)g.w + g.geom.scale_offset()) : nullptr;
-    skinny_bf16_kernel<MT, U, NPB, EPI, SPLIT, OutT, W8><<<grid, dim3(SK_THREADS), 0, s>>>(
+    const void* scales = WF != WF_BF16 ? (const uint8_t*)g.w + g.geom.scale_offset() : nullptr;
+    skinny_bf16_kernel<MT, U, NPB, EPI, SPLIT, OutT, WF><<<grid, dim3(SK_THREADS), 0, s>>>(
         (const uint16_t*)g.a, g.lda, g.geom.K, (const i32x4*)g.w, g.geom.nkc, p.chunks_per_split,
         (OutT*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M, scales,
         (const OutT*)g.resid, g.ldr, (const OutT*)g.bias);
 }
 
-template <int MT, int U, int NPB, int EPI, bool W8>
+template <int MT, int U, int NPB, int EPI, int WF>
 static void pick_split_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     if (p.splits > 1)
-        go_bf16<MT, U, NPB, EPI, true, uint16_t, W8>(g, p, partial, s);
+        go_bf16<MT, U, NPB, EPI, true, uint16_t, WF>(g, p, partial, s);
     else
-        go_bf16<MT, U, NPB, EPI, false, uint16_t, W8>(g, p, partial, s);
+        go_bf16<MT, U, NPB, EPI, false, uint16_t, WF>(g, p, partial, s);
 }
 
 // Loads in flight per lane: 2*NPB*U weight pieces plus U*MT activation
 // fragments (times two with FP8 weights), measured on the 8B- and
 // 72B-class decode shapes.
-template <int EPI, bool W8>
+template <int EPI, int WF>
 static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
+    // FP8 and MXFP4 pieces already span 64 and 128 K: fewer in flight; the
+    // MXFP4 activation fragments (4 per piece and row tile) bound U above
+    // two row tiles
+    constexpr bool Q = WF != WF_BF16;
     switch (p.row_tile / 16) {
     case 1:
-        if (W8)   // a piece already spans 64 K: two in flight per half suffice
-            pick_split_bf16<1, 2, 2, EPI, W8>(g, p, partial, s);
-        else if (p.pb_per_wg == 2)
-            pick_split_bf16<1, 4, 2, EPI, W8>(g, p, partial, s);
-        else if (g.M > 4)
-            pick_split_bf16<1, 4, 1, EPI, W8>(g, p, partial, s);
-        else
-            pick_split_bf16<1, 8, 1, EPI, W8>(g, p, partial, s);
+        if constexpr (Q) {
+            pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
+        } else {
+            if (p.pb_per_wg == 2)
+                pick_split_bf16<1, 4, 2, EPI, WF>(g, p, partial, s);
+            else if (g.M > 4)
+                pick_split_bf16<1, 4, 1, EPI, WF>(g, p, partial, s);
+            else
+                pick_split_bf16<1, 8, 1, EPI, WF>(g, p, partial, s);
+        }
         break;
-    case 2: pick_split_bf16<2, 4, 2, EPI, W8>(g, p, partial, s); break;
-    case 3: pick_split_bf16<3, 2, 2, EPI, W8>(g, p, partial, s); break;
-    default: pick_split_bf16<4, 2, 2, EPI, W8>(g, p, partial, s); break;
+    case 2: pick_split_bf16<2, Q ? 2 : 4, 2, EPI, WF>(g, p, partial, s); break;
+    case 3: pick_split_bf16<3, WF == WF_MXFP4 ? 1 : 2, 2, EPI, WF>(g, p, partial, s); break;
+    default: pick_split_bf16<4, WF == WF_MXFP4 ? 1 : 2, 2, EPI, WF>(g, p, partial, s); break;
     }
 }
 
@@ -481,14 +524,19 @@ hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial,
 {
     if (g.dt == DT_BF16) {
         if (g.epi == EPI_SWIGLU)
-            pick_mt_bf16<EPI_SWIGLU, false>(g, p, partial, s);
+            pick_mt_bf16<EPI_SWIGLU, WF_BF16>(g, p, partial, s);
         else
-            pick_mt_bf16<EPI_PLAIN, false>(g, p, partial, s);
+            pick_mt_bf16<EPI_PLAIN, WF_BF16>(g, p, partial, s);
     } else if (g.dt == DT_FP8W) {
         if (g.epi == EPI_SWIGLU)
-            pick_mt_bf16<EPI_SWIGLU, true>(g, p, partial, s);
+            pick_mt_bf16<EPI_SWIGLU, WF_FP8>(g, p, partial, s);
         else
-            pick_mt_bf16<EPI_PLAIN, true>(g, p, partial, s);
+            pick_mt_bf16<EPI_PLAIN, WF_FP8>(g, p, partial, s);
+    } else if (g.dt == DT_MXFP4W) {
+        if (g.epi == EPI_SWIGLU)
+            pick_mt_bf16<EPI_SWIGLU, WF_MXFP4>(g, p, partial, s);
+        else
+            pick_mt_bf16<EPI_PLAIN, WF_MXFP4>(g, p, partial, s);
     } else {
         if (g.epi == EPI_SWIGLU)
             pick_rt_f32<EPI_SWIGLU>(g, p, partial, s);

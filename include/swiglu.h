@@ -20,8 +20,9 @@
  *     captured with).
  *   - dtype is SWIGLU_BF16 (bf16 storage, fp32 accumulation, bf16 output)
  *     or SWIGLU_F32 (fp32 storage and arithmetic): x, the weights and the
- *     output share that dtype.  Or SWIGLU_BF16_FP8W: x, out and y in bf16,
- *     weights stored as 8-bit floats (see below), fp32 accumulation.
+ *     output share that dtype.  Or SWIGLU_BF16_FP8W / SWIGLU_BF16_MXFP4W: x,
+ *     out and y in bf16, weights stored as 8-bit or 4-bit floats (see
+ *     below), fp32 accumulation.
  *   - Calls only enqueue kernels on `stream` (the graph-creation calls
  *     excepted): no allocation, no copy, no
  *     synchronisation (the decode-path conventions of "Où part le temps d'un
@@ -69,7 +70,21 @@ typedef enum swiglu_dtype {
      * SWIGLU_ERR_UNSUPPORTED.  The packed buffers hold the codes (one byte
      * per weight, padded like bf16) followed by the fp32 column scales.
      */
-    SWIGLU_BF16_FP8W = 2
+    SWIGLU_BF16_FP8W = 2,
+    /*
+     * MXFP4 weights for decode, the same idea at four bits: OCP Microscaling
+     * (v1.0) MXFP4, E2M1 codes with one power-of-two (E8M0) scale per 32
+     * consecutive rows of a column.  The pack calls take bf16 weights: the
+     * block's shared exponent is floor(log2(largest magnitude)) - 2,
+     * clamped to [-126, 127] (0 for an all-zero block), and each code is
+     * the E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to w / 2^s, ties
+     * to the even code, saturating at 6.  The kernels widen codes and scale
+     * exactly to bf16 (gfx950's scaled FP4 conversion), multiply on the
+     * matrix unit with fp32 accumulation.  Skinny path only, like
+     * SWIGLU_BF16_FP8W; K is padded to 128 and the packed buffers hold half
+     * a byte per weight plus one scale byte per 32 weights.
+     */
+    SWIGLU_BF16_MXFP4W = 3
 } swiglu_dtype_t;
 
 typedef enum swiglu_status {

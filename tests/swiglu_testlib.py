@@ -12,7 +12,7 @@ import workloads as wl
 
 # FP8 weights: bf16 outputs of fp32 sums over exactly widened codes, so the
 # bf16 bar applies against the oracle's product with the same codes.
-TOL = {wl.F32: 1e-4, wl.BF16: 2e-2, wl.FP8W: 2e-2}
+TOL = {wl.F32: 1e-4, wl.BF16: 2e-2, wl.FP8W: 2e-2, wl.MXFP4W: 2e-2}
 
 
 def say(*args):

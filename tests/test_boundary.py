@@ -184,3 +184,14 @@ def test_mlp_block_arguments_and_workspace():
                need - 256) == sw.SWIGLU_ERR_WORKSPACE
     assert sw.mlp_block_forward_ex(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, M, d, dff, F32, FAKE,
                                    need, 0, sw.SWIGLU_PATH_WIDE) == sw.SWIGLU_ERR_UNSUPPORTED
+
+
+def test_mxfp4_weight_sizes_and_paths():
+    W4 = sw.SWIGLU_BF16_MXFP4W
+    # half a byte per weight (K padded to 128), one scale byte per 32 weights
+    assert sw.swiglu_packed_bytes(4096, 14336, W4) == 4096 * 14336 + 4096 * 14336 * 2 // 32
+    assert sw.swiglu_packed_bytes(136, 40, W4) == 256 * 128 + 256 * 128 * 2 // 32
+    for M in (1, 64, 65):
+        assert sw.swiglu_select_path(M, 4096, 14336, W4) == sw.SWIGLU_PATH_SKINNY
+    rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, W4, None, 0, 0, sw.SWIGLU_PATH_WIDE)
+    assert rc == sw.SWIGLU_ERR_UNSUPPORTED

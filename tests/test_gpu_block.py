@@ -12,7 +12,7 @@ from swiglu_testlib import assert_close, bytes_buf, dev, empty, host, pack, say,
 
 pytestmark = pytest.mark.gpu
 
-BF16, F32, W8 = wl.BF16, wl.F32, wl.FP8W
+BF16, F32, W8, W4 = wl.BF16, wl.F32, wl.FP8W, wl.MXFP4W
 EPS = 1e-6
 
 
@@ -44,6 +44,8 @@ def _reference(inp, dtype, bias=True):
     w = {k: inp[k] for k in ("wg", "wu", "wd")}
     if dtype == W8:
         w = {k: oracle.dequantize_e4m3(*oracle.quantize_e4m3(v)) for k, v in w.items()}
+    if dtype == W4:
+        w = {k: oracle.dequantize_mxfp4(*oracle.quantize_mxfp4(v)) for k, v in w.items()}
     return oracle.mlp_block(inp["r"], inp["gamma"], EPS, w["wg"], w["wu"], w["wd"],
                             bias=inp["bias"] if bias else None)
 
@@ -53,6 +55,7 @@ CASES = [
     (130, 264, 712, BF16, 0), (300, 1000, 1400, BF16, 0), (96, 512, 1408, BF16, 1),
     (4, 100, 60, F32, 0), (12, 64, 520, F32, 0),
     (16, 1032, 776, W8, 0), (64, 896, 4864, W8, 0),
+    (16, 1032, 776, W4, 0), (64, 896, 4864, W4, 0),
 ]
 
 

@@ -63,6 +63,28 @@ def test_mlp_workload(name):
     say(name, st)
 
 
+@pytest.mark.parametrize("name", ["decode8b_m1_mxfp4w", "decode8b_m16_mxfp4w", "mlp72b_m16_mxfp4w"])
+def test_mxfp4w_workload(name):
+    # MXFP4 weights at the decode shapes against the oracle's product with
+    # its own quantisation of the same bf16 weights (the packer's codes and
+    # scales equal it bit for bit: test_gpu_mxfp4.py)
+    w = wl.WORKLOADS[name]
+    say("workload", name, w)
+    inp = wl.make_inputs(w, M=w.M)
+    wp, wdp = pack(inp, w.d, w.dff, w.dtype)
+    deq = {k: oracle.dequantize_mxfp4(*oracle.quantize_mxfp4(inp[k]))
+           for k in ("wg", "wu", "wd") if k in inp}
+    x64 = oracle.to_double(inp["x"])
+    if w.with_down:
+        out = run_mlp(dev(inp["x"]), wp, wdp, w.M, w.d, w.dff, w.dtype)
+        ref = oracle.mlp(x64, deq["wg"], deq["wu"], deq["wd"])
+    else:
+        out = run_up(dev(inp["x"]), wp, w.M, w.d, w.dff, w.dtype)
+        ref = oracle.swiglu(x64, deq["wg"], deq["wu"])
+    st = assert_close(host(out, w.dtype), ref, w.dtype, name)
+    say(name, st)
+
+
 @pytest.mark.parametrize("name", ["decode8b_m1_fp8w", "decode8b_m16_fp8w", "mlp72b_m16_fp8w"])
 def test_fp8w_workload(name):
     # FP8 weights at the decode shapes: reference = the oracle's product with

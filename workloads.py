@@ -20,7 +20,8 @@ import numpy as np
 F32 = 0
 BF16 = 1
 FP8W = 2     # bf16 activations; weights packed as E4M3 codes (drawn here in bf16)
-DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8W: "bf16-fp8w"}
+MXFP4W = 3   # bf16 activations; weights packed as MXFP4 (drawn here in bf16)
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8W: "bf16-fp8w", MXFP4W: "bf16-mxfp4w"}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -41,19 +42,24 @@ class Workload:
         return 4 if self.dtype == F32 else 2
 
     @property
-    def weight_bytes(self) -> int:
-        """Bytes per stored weight."""
-        return 1 if self.dtype == FP8W else self.elem_bytes
+    def weight_bytes(self) -> float:
+        """Bytes per stored weight (half a byte for MXFP4)."""
+        return {FP8W: 1, MXFP4W: 0.5}.get(self.dtype, self.elem_bytes)
+
+    def _weight_matrix_bytes(self, K: int, N: int) -> int:
+        if self.dtype == FP8W:       # codes and one fp32 scale per column
+            return K * N + 4 * N
+        if self.dtype == MXFP4W:     # half-byte codes and one scale byte per 32
+            return K * N // 2 + K * N // 32
+        return K * N * self.elem_bytes
 
     def algorithmic_bytes(self) -> int:
-        """Bytes the method must move: weights once (with their fp32 column
-        scales when stored as FP8), x once, output once."""
-        s, ws = self.elem_bytes, self.weight_bytes
-        b = 2 * self.d * self.dff * ws + self.M * self.d * s
-        if self.dtype == FP8W:
-            b += 2 * self.dff * 4 + (self.d * 4 if self.with_down else 0)
+        """Bytes the method must move: weights once (with their scales when
+        quantised), x once, output once."""
+        s = self.elem_bytes
+        b = 2 * self._weight_matrix_bytes(self.d, self.dff) + self.M * self.d * s
         if self.with_down:
-            b += self.dff * self.d * ws + self.M * self.d * s
+            b += self._weight_matrix_bytes(self.dff, self.d) + self.M * self.d * s
         else:
             b += self.M * self.dff * s
         return b
@@ -85,6 +91,9 @@ WORKLOADS = {
     "decode8b_m1_fp8w": _wl(2, "decode8b_m1_fp8w", 1, 4096, 14336, FP8W, False, 16),
     "decode8b_m16_fp8w": _wl(2, "decode8b_m16_fp8w", 16, 4096, 14336, FP8W, False, 16),
     "mlp72b_m16_fp8w": _wl(5, "mlp72b_m16_fp8w", 16, 8192, 29568, FP8W, True, 2048),
+    "decode8b_m1_mxfp4w": _wl(2, "decode8b_m1_mxfp4w", 1, 4096, 14336, MXFP4W, False, 16),
+    "decode8b_m16_mxfp4w": _wl(2, "decode8b_m16_mxfp4w", 16, 4096, 14336, MXFP4W, False, 16),
+    "mlp72b_m16_mxfp4w": _wl(5, "mlp72b_m16_mxfp4w", 16, 8192, 29568, MXFP4W, True, 2048),
 }
 
 # tensor ids used in seeds: seed = 1000 * cfg + id
