@@ -455,6 +455,8 @@ static void pick_split_bf16(const GemmArgs& g, const SkinnyPlan& p, float* parti
 // Loads in flight per lane: 2*NPB*U weight pieces plus U*MT activation
 // fragments (times two with FP8 weights), measured on the 8B- and
 // 72B-class decode shapes.
+constexpr int64_t MXFP4_WIDE_PB_CUS = 256;   // MI355X compute units
+
 template <int EPI, int WF>
 static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
@@ -464,7 +466,15 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     constexpr bool Q = WF != WF_BF16;
     switch (p.row_tile / 16) {
     case 1:
-        if constexpr (Q) {
+        if constexpr (WF == WF_MXFP4) {
+            // one piece in flight per half; above 8 rows, four pair blocks
+            // per wave when that still leaves a workgroup per CU (measured
+            // at 1, 8 and 16 rows on the 8B and 72B shapes)
+            if (g.M > 8 && p.grid_pb >= 4 * MXFP4_WIDE_PB_CUS)
+                pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
+            else
+                pick_split_bf16<1, 1, 2, EPI, WF>(g, p, partial, s);
+        } else if constexpr (Q) {
             pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
         } else {
             if (p.pb_per_wg == 2)
