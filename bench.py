@@ -276,7 +276,7 @@ def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float) -> dict:
 def probe() -> int:
     """Kernels for hardware-counter runs: a plain copy of known size (reads
     and writes exactly 1 GiB) to calibrate FETCH_SIZE / WRITE_SIZE, then the
-    decode (bf16 and FP8 weights) and prefill steps as the bench runs them."""
+    decode (bf16, FP8 and MXFP4 weights) and prefill steps as the bench runs them."""
     import torch
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -286,7 +286,8 @@ def probe() -> int:
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
-    for name, steps in (("decode8b_m1", 5), ("decode8b_m1_fp8w", 5), ("prefill8b_m4096", 3)):
+    for name, steps in (("decode8b_m1", 5), ("decode8b_m1_fp8w", 5), ("decode8b_m1_mxfp4w", 5),
+                        ("prefill8b_m4096", 3)):
         w = wl.WORKLOADS[name]
         r = Runner(w, 5 if w.M == 1 else 1)
         for i in range(steps):
@@ -307,6 +308,8 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the FP8- and MXFP4-weight decode lines")
     ap.add_argument("--block", action="store_true",
                     help="time the MLP block (RMSNorm, MLP, bias and residual) on a workload "
                          "with the down projection")
@@ -364,6 +367,25 @@ def main() -> int:
     m["runner"].close()
     del m
     torch.cuda.empty_cache()
+    if not args.no_variants and w.name == "decode8b_m1":
+        # the same decode step with quantised weights (packed from the same
+        # bf16 weights); reported beside the bf16 headline, never as it
+        rec["quantized_decode"] = {}
+        for name in ("decode8b_m1_fp8w", "decode8b_m1_mxfp4w"):
+            q = wl.WORKLOADS[name]
+            qcopies = max(1, -(-(1 << 30) // int(2 * q.d * q.dff * q.weight_bytes)))
+            mq = measure(q, args.steps, args.warmup, qcopies)
+            tq = mq["timing"]
+            rec["quantized_decode"][name] = {
+                "dtype": wl.DTYPE_NAMES[q.dtype],
+                "value": round(q.algorithmic_bytes() / (tq["wall_ms_per_step"] * 1e-3) / 1e9, 1),
+                "unit": "GB/s", "ms_per_step": round(tq["wall_ms_per_step"], 5),
+                "algorithmic_bytes": q.algorithmic_bytes(), "roofline": mq["roofline"],
+                "timing_ms": {k: round(v, 5) for k, v in tq.items()},
+            }
+            mq["runner"].close()
+            del mq
+            torch.cuda.empty_cache()
     if not args.no_prefill and w.name != "prefill8b_m4096":
         p = wl.WORKLOADS["prefill8b_m4096"]
         mp = measure(p, args.prefill_steps, args.prefill_warmup, 1)
