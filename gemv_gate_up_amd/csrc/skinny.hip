@@ -414,8 +414,12 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
     const int64_t target =
         (g.epi == EPI_SWIGLU && p.row_tile > 16) ? (int64_t)num_cus : 2 * (int64_t)num_cus;
     const int64_t min_chunks = 8;
+    // A split costs a second launch of a few microseconds: not worth it when
+    // each pair block streams little (the tiny fp32 decode, 64 KB per pair
+    // block: 7.1 us with a 4-way split and its second pass, 5.1 us without).
+    const bool small = g.geom.bytes() < (int64_t)128 * 1024 * p.grid_pb;
     int64_t S = 1;
-    while (base * S < target && g.geom.nkc / (2 * S) >= min_chunks && S < 64)
+    while (!small && base * S < target && g.geom.nkc / (2 * S) >= min_chunks && S < 64)
         S *= 2;
     p.chunks_per_split = ceil_div(g.geom.nkc, S);
     p.splits = (int)ceil_div(g.geom.nkc, p.chunks_per_split);

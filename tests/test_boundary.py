@@ -57,8 +57,11 @@ def test_dispatcher():
 def test_workspace_sizes():
     # decode: the pair blocks fill the GPU, no split-K partials needed
     assert sw.swiglu_workspace_bytes(1, 4096, 14336, BF16, 0) == 0
-    # tiny fp32 decode splits K four ways: 4 x 1 x 4096 fused columns x 4 B
-    assert sw.swiglu_workspace_bytes(1, 512, 2048, F32, 0) == 4 * 4096 * 4
+    # the tiny fp32 decode streams 64 KB per pair block: not worth a split
+    assert sw.swiglu_workspace_bytes(1, 512, 2048, F32, 0) == 0
+    # a long K over 512 columns (32 pair blocks, 512 KB each) splits it 16
+    # ways: 16 slices x 1 row x 1024 packed columns x 4 B of partials
+    assert sw.swiglu_workspace_bytes(1, 4096, 512, F32, 0) == 16 * 1024 * 4
     # full MLP keeps h (M x padded dff) in the workspace
     assert sw.swiglu_workspace_bytes(2048, 8192, 29568, BF16, 1) >= 2048 * 29568 * 2
     assert sw.swiglu_workspace_bytes_ex(4096, 512, 2048, F32, 0, sw.SWIGLU_PATH_WIDE) == 0
@@ -89,8 +92,8 @@ def test_argument_errors_return_before_any_launch(dtype):
 
 
 def test_workspace_too_small_is_rejected():
-    # tiny fp32 decode needs split-K partials; none are given
-    rc = sw.swiglu_up(FAKE, FAKE, FAKE, 1, 512, 2048, F32, None, 0, stream=0)
+    # a split-K decode needs partials; none are given
+    rc = sw.swiglu_up(FAKE, FAKE, FAKE, 1, 4096, 512, F32, None, 0, stream=0)
     assert rc == sw.SWIGLU_ERR_WORKSPACE
     need = sw.swiglu_workspace_bytes(64, 896, 4864, BF16, 1)
     rc = sw.mlp_forward(FAKE, FAKE, FAKE, FAKE, 64, 896, 4864, BF16, FAKE, need - 256, stream=0)
@@ -124,7 +127,7 @@ def test_graph_create_rejects_bad_arguments_before_any_hip_call():
     assert (rc, h) == (sw.SWIGLU_ERR_INVALID_ARG, None)
     rc, h = sw.swiglu_up_graph_create(FAKE + 4, FAKE, FAKE, 4, 64, 64, BF16)
     assert (rc, h) == (sw.SWIGLU_ERR_MISALIGNED, None)
-    rc, h = sw.swiglu_up_graph_create(FAKE, FAKE, FAKE, 1, 512, 2048, F32, None, 0)
+    rc, h = sw.swiglu_up_graph_create(FAKE, FAKE, FAKE, 1, 4096, 512, F32, None, 0)
     assert (rc, h) == (sw.SWIGLU_ERR_WORKSPACE, None)
     rc, h = sw.swiglu_up_graph_create(FAKE, FAKE, FAKE, 4, 64, 64, F32, None, 0,
                                       sw.SWIGLU_PATH_WIDE)

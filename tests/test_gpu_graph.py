@@ -18,6 +18,7 @@ AUTO, PHASED = sw.SWIGLU_PATH_AUTO, sw.SWIGLU_PATH_WIDE_PHASED
 # (M, d, dff, dtype, with_down, path): split-K skinny with its reduce kernel,
 # the 4-launch small MLP, the wide kernels, and the fp32 skinny path
 CASES = [
+    (1, 4096, 512, F32, False, AUTO),
     (1, 512, 2048, F32, False, AUTO),
     (64, 896, 4864, BF16, True, AUTO),
     (16, 1024, 1408, BF16, True, AUTO),

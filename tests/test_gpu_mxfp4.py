@@ -117,7 +117,7 @@ def test_exact_grid_weights_give_exact_products():
 
 
 def test_mxfp4_split_path_and_refused_wide_paths():
-    M, d, dff = 1, 4096, 512
+    M, d, dff = 1, 16384, 512
     assert sw.swiglu_workspace_bytes(M, d, dff, W4, 0) > 0
     inp = wl.random_inputs(78, M, d, dff, W4)
     wp, _ = pack(inp, d, dff, W4)
