@@ -401,6 +401,8 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
     SkinnyPlan p;
     p.grid_pb = ceil_div(g.ncols_out, g.geom.cols_per_pb);
     p.pb_per_wg = g.dt != DT_F32 ? bf16_pair_blocks(g.M, g.dt) : 1;
+    if (g.dt != DT_F32 && g.epi == EPI_PLAIN && g.M > 16)
+        p.pb_per_wg = 1;
     p.row_tile = g.dt != DT_F32 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M);
     p.row_groups = ceil_div(g.M, p.row_tile);
     // Split K only when there are too few pair blocks (units of weight
@@ -413,7 +415,9 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
     const int64_t base = p.grid_pb * p.row_groups;
     const int64_t target =
         (g.epi == EPI_SWIGLU && p.row_tile > 16) ? (int64_t)num_cus : 2 * (int64_t)num_cus;
-    const int64_t min_chunks = 8;
+    // each slice streams at least 16 pieces (the 0.5B-class MLP's down
+    // product at 64 rows: 19 pieces per slice 11.9 us, 9.5 pieces 13.5 us)
+    const int64_t min_chunks = 16;
     // A split costs a second launch of a few microseconds: not worth it when
     // each pair block streams little (the tiny fp32 decode, 64 KB per pair
     // block: 7.1 us with a 4-way split and its second pass, 5.1 us without).
@@ -489,9 +493,11 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
                 pick_split_bf16<1, 8, 1, EPI, WF>(g, p, partial, s);
         }
         break;
-    case 2: pick_split_bf16<2, Q ? 2 : 4, 2, EPI, WF>(g, p, partial, s); break;
-    case 3: pick_split_bf16<3, WF == WF_MXFP4 ? 1 : 2, 2, EPI, WF>(g, p, partial, s); break;
-    default: pick_split_bf16<4, WF == WF_MXFP4 ? 1 : 2, 2, EPI, WF>(g, p, partial, s); break;
+    // above 16 rows a plain (down) product takes one pair block per wave:
+    // its few 32-column blocks are better spread over more workgroups
+    case 2: pick_split_bf16<2, Q ? 2 : 4, EPI == EPI_PLAIN ? 1 : 2, EPI, WF>(g, p, partial, s); break;
+    case 3: pick_split_bf16<3, WF == WF_MXFP4 ? 1 : 2, EPI == EPI_PLAIN ? 1 : 2, EPI, WF>(g, p, partial, s); break;
+    default: pick_split_bf16<4, WF == WF_MXFP4 ? 1 : 2, EPI == EPI_PLAIN ? 1 : 2, EPI, WF>(g, p, partial, s); break;
     }
 }
 
