@@ -306,7 +306,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode8b_m1", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--prefill-warmup", type=int, default=10)
+    ap.add_argument("--prefill-warmup", type=int, default=40,
+                    help="untimed prefill steps first: the clock needs ~30 ms of matrix work to settle")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the FP8- and MXFP4-weight decode lines")
