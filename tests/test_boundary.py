@@ -198,3 +198,22 @@ def test_mxfp4_weight_sizes_and_paths():
         assert sw.swiglu_select_path(M, 4096, 14336, W4) == sw.SWIGLU_PATH_SKINNY
     rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, W4, None, 0, 0, sw.SWIGLU_PATH_WIDE)
     assert rc == sw.SWIGLU_ERR_UNSUPPORTED
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # a C99 program against include/swiglu.h, linked with libswiglu.so; it
+    # exercises argument checks only, so it runs without a GPU
+    import os
+    src = os.path.join(os.path.dirname(__file__), "c", "abi_check.c")
+    exe = str(tmp_path / "abi_check")
+    libdir = os.path.dirname(sw.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.dirname(sw.HEADER_PATH), "-I", "/opt/rocm/include", src, "-o", exe,
+           "-L", libdir, "-lswiglu", "-Wl,-rpath," + libdir]
+    subprocess.run(["ln", "-sf", sw.LIB_PATH, str(tmp_path / "libswiglu.so")], check=True)
+    cmd[cmd.index("-L") + 1] = str(tmp_path)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_check ok" in r.stdout
