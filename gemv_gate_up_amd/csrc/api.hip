@@ -6,7 +6,8 @@
 // left operand has at most 16 rows; ours extends it to 64 rows by giving
 // each wave up to four 16-row MFMA tiles); more rows go to the fused MFMA
 // GEMM ("Tile-Level Activation Overlap for Efficient LLM Inference" picks
-// between its two kernels by batch size in the same way).
+// between its two kernels by batch size in the same way).  fp32, FP8 and
+// MXFP4 weights always take the split-over-weights kernels.
 #include <stdint.h>
 #include <string.h>
 
@@ -25,6 +26,8 @@ namespace {
 
 constexpr int64_t MAX_DIM = (int64_t)1 << 20;
 constexpr int64_t MAX_M = (int64_t)1 << 18;
+// skinny/wide crossover, measured with both paths forced: skinny wins up to
+// 80 rows on the 8B-class shape, wide from 64 rows on the 72B-class shape
 constexpr int64_t SKINNY_MAX_M_BF16 = 64;
 constexpr int TARGET_CUS = 256;   // MI355X compute units: split-K planning target
 constexpr size_t WS_ALIGN = 256;
@@ -305,18 +308,18 @@ int record_graph(Call&& call, swiglu_graph_t* out)
     hipGraphExec_t exec = nullptr;
     if (rc == SWIGLU_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
         rc = SWIGLU_ERR_HIP;
-    hipStreamDestroy(s);
+    (void)hipStreamDestroy(s);
     swiglu_graph_s* h = nullptr;
     if (rc == SWIGLU_OK) {
         h = new (std::nothrow) swiglu_graph_s{graph, exec};
         if (!h) {
-            hipGraphExecDestroy(exec);
+            (void)hipGraphExecDestroy(exec);
             rc = SWIGLU_ERR_HIP;
         }
     }
     if (rc != SWIGLU_OK) {
         if (graph)
-            hipGraphDestroy(graph);
+            (void)hipGraphDestroy(graph);
         return rc;
     }
     *out = h;
@@ -509,8 +512,8 @@ int swiglu_graph_destroy(swiglu_graph_t graph)
 {
     if (!graph)
         return SWIGLU_OK;
-    hipGraphExecDestroy(graph->exec);
-    hipGraphDestroy(graph->graph);
+    (void)hipGraphExecDestroy(graph->exec);
+    (void)hipGraphDestroy(graph->graph);
     delete graph;
     return SWIGLU_OK;
 }

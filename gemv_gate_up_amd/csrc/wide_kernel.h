@@ -70,14 +70,16 @@ __device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t num_bytes) 
 // 16 bytes per lane, global -> LDS at lds_base + 16 * lane, bypassing VGPRs;
 // the address is base + voffset (per lane) + soffset (per wave, the K step).
 // Issued through inline asm so that the compiler does not add a blanket
-// vmcnt(0) before LDS reads; completion is awaited with wait_vmcnt.  A lane
-// whose voffset alone is past num_records reads zero whatever soffset is.
+// vmcnt(0) before LDS reads; completion is awaited with wait_vmcnt.  The LDS
+// base goes in through M0 as an operand, so the compiler writes M0 itself
+// and knows its value.  A lane whose voffset alone is past num_records reads
+// zero whatever soffset is.
 __device__ __forceinline__ void load_lds16(const i32x4& srd, uint32_t voffset, uint32_t soffset,
                                            uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "v"(voffset), "s"(srd), "s"(soffset), "s"(lds_base)
-                 : "memory", "m0");
+                 : "v"(voffset), "s"(srd), "s"(soffset), "{m0}"(lds_base)
+                 : "memory");
 }
 
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, bool PHASED = false>

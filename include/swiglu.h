@@ -29,7 +29,9 @@
  *     token": fixed buffers, no per-call allocation, no host waits).  A
  *     return of SWIGLU_OK means the arguments were valid and the launches
  *     were accepted; faults during execution surface at the caller's next
- *     synchronisation.
+ *     synchronisation.  Launch errors are read with hipGetLastError, so
+ *     SWIGLU_ERR_HIP also reports (and clears) an error that an earlier HIP
+ *     call of the calling thread left pending.
  *   - Results are deterministic: the same inputs, shapes and device give
  *     bitwise identical outputs on every call (no atomics in any sum).
  *   - Errors are returned as negative status codes; nothing throws.  When
