@@ -1,19 +1,23 @@
-// skinny.hip -- the few-rows (decode) path: out = epi(A . W) for M <= 64.
+// skinny.hip -- the few-rows (decode) path: out = epi(A . W), built for up
+// to 64 rows (the dispatcher's range for bf16); fp32, FP8 and MXFP4 weights
+// use it at any M, 64 rows per row group.
 //
 // Follows the split-over-the-weights idea of "Où part le temps d'un token"
 // (section "Un kernel pour les matrices étroites"): with only a few rows of
 // activations the grid is cut along the weights, which are large, not along
-// the output, which is small.  Each workgroup owns one pair block of the
-// packed weights (16 gate + 16 up columns, or 32 down columns) and a range
-// of K; its four waves take interleaved K chunks, each lane streaming
-// 16-byte nontemporal loads with several in flight.  Partial sums of the
+// the output, which is small.  Each workgroup owns one to four consecutive
+// pair blocks of the packed weights (16 gate + 16 up columns, or 32 down
+// columns, each) and a range of K; its four waves take interleaved K
+// pieces, each lane streaming 16-byte nontemporal loads with several in
+// flight.  Partial sums of the
 // waves are combined in LDS in a fixed order.  When the pair blocks alone
 // do not fill the GPU, K is also split across workgroups and a second pass
 // adds the slices in ascending order; no atomics are used, so results are
 // reproducible run to run (same section: the authors reject an atomic add
 // into the output for that reason).  silu(g) * u is applied once the full
 // K sum is known (the second pass or the LDS combine), like the bias of the
-// "Affine" operation in "Deux opérations de trop".
+// "Affine" operation in "Deux opérations de trop"; a down product adds its
+// optional bias and residual at the same point.
 //
 // bf16 weights are multiplied on v_mfma_f32_16x16x32_bf16 with the
 // activations as the 16-row A operand: at M <= 16 the matrix unit has spare
