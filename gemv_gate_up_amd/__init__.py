@@ -81,6 +81,8 @@ _SIGS = {
                                       ctypes.POINTER(_vp)]),
     "mlp_forward_graph_create": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz,
                                         _int, ctypes.POINTER(_vp)]),
+    "mlp_block_graph_create": (_int, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _i64, _i64,
+                                      _i64, _int, _vp, _sz, _int, ctypes.POINTER(_vp)]),
     "swiglu_graph_launch": (_int, [_vp, _vp]),
     "mlp_block_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
     "mlp_block_workspace_bytes_ex": (_sz, [_i64, _i64, _i64, _int, _int]),
@@ -220,6 +222,16 @@ def mlp_forward_graph_create(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspac
     rc = _lib.mlp_forward_graph_create(_ptr(x), _ptr(Wpacked), _ptr(Wdpacked), _ptr(y), M, d,
                                        dff, dtype, _ptr(workspace), workspace_bytes, path,
                                        ctypes.byref(h))
+    return rc, h.value
+
+
+def mlp_block_graph_create(r, gamma, eps, Wpacked, Wdpacked, bias, out, M, d, dff, dtype,
+                           workspace=None, workspace_bytes=0, path=SWIGLU_PATH_AUTO):
+    """Returns (status, handle); the handle (an int) is None unless status is 0."""
+    h = _vp()
+    rc = _lib.mlp_block_graph_create(_ptr(r), _ptr(gamma), eps, _ptr(Wpacked), _ptr(Wdpacked),
+                                     _ptr(bias), _ptr(out), M, d, dff, dtype, _ptr(workspace),
+                                     workspace_bytes, path, ctypes.byref(h))
     return rc, h.value
 
 

@@ -501,6 +501,19 @@ int mlp_forward_graph_create(const void* x, const void* Wpacked, const void* Wdp
         graph);
 }
 
+int mlp_block_graph_create(const void* r, const void* gamma, float eps, const void* Wpacked,
+                           const void* Wdpacked, const void* bias, void* out, int64_t M, int64_t d,
+                           int64_t dff, int dtype, void* workspace, size_t workspace_bytes,
+                           int path, swiglu_graph_t* graph)
+{
+    return record_graph(
+        [&](hipStream_t s, bool launch) {
+            return do_block(r, gamma, eps, Wpacked, Wdpacked, bias, out, M, d, dff, dtype,
+                            workspace, workspace_bytes, s, path, launch);
+        },
+        graph);
+}
+
 int swiglu_graph_launch(swiglu_graph_t graph, hipStream_t stream)
 {
     if (!graph)

@@ -247,9 +247,10 @@ int mlp_block_forward_ex(const void *r, const void *gamma, float eps, const void
  * (and the weights, if they change) in place and launch again; out/y are
  * rewritten by each launch.
  *
- * swiglu_up_graph_create / mlp_forward_graph_create validate their
- * arguments exactly as swiglu_up_ex / mlp_forward_ex do (same status
- * codes; nothing is created on error), then record that one call on a
+ * swiglu_up_graph_create / mlp_forward_graph_create / mlp_block_graph_create
+ * validate their arguments exactly as swiglu_up_ex / mlp_forward_ex /
+ * mlp_block_forward_ex do (same status codes; nothing is created on
+ * error), then record that one call on a
  * private stream of the current device and instantiate it.  They allocate
  * host and HIP objects, so they belong to set-up, not to the per-call path.
  * On success *graph receives a handle owned by the caller; the buffers must
@@ -273,6 +274,12 @@ int mlp_forward_graph_create(const void *x, const void *Wpacked, const void *Wdp
                              int64_t M, int64_t d, int64_t dff, int dtype,
                              void *workspace, size_t workspace_bytes, int path,
                              swiglu_graph_t *graph);
+
+int mlp_block_graph_create(const void *r, const void *gamma, float eps, const void *Wpacked,
+                           const void *Wdpacked, const void *bias, void *out,
+                           int64_t M, int64_t d, int64_t dff, int dtype,
+                           void *workspace, size_t workspace_bytes, int path,
+                           swiglu_graph_t *graph);
 
 int swiglu_graph_launch(swiglu_graph_t graph, hipStream_t stream);
 

@@ -43,6 +43,8 @@ int main(void)
     CHECK(swiglu_up_graph_create(fake, fake, fake, -1, 64, 64, SWIGLU_BF16, NULL, 0,
                                  SWIGLU_PATH_AUTO, &g) == SWIGLU_ERR_INVALID_ARG);
     CHECK(g == NULL);
+    CHECK(mlp_block_graph_create(fake, fake, -1.0f, fake, fake, NULL, fake, 4, 64, 64, SWIGLU_BF16,
+                                 fake, 1 << 20, SWIGLU_PATH_AUTO, &g) == SWIGLU_ERR_INVALID_ARG);
     CHECK(swiglu_graph_launch(NULL, NULL) == SWIGLU_ERR_INVALID_ARG);
     CHECK(swiglu_graph_destroy(NULL) == SWIGLU_OK);
     puts("abi_check ok");

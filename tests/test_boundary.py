@@ -136,6 +136,9 @@ def test_graph_create_rejects_bad_arguments_before_any_hip_call():
     assert (rc, h) == (sw.SWIGLU_ERR_INVALID_ARG, None)
     assert sw._lib.swiglu_up_graph_create(FAKE, FAKE, FAKE, 4, 64, 64, BF16, None, 0, 0,
                                           None) == sw.SWIGLU_ERR_INVALID_ARG
+    rc, h = sw.mlp_block_graph_create(FAKE, FAKE, -1.0, FAKE, FAKE, None, FAKE, 4, 64, 64, BF16,
+                                      FAKE, 1 << 20)
+    assert (rc, h) == (sw.SWIGLU_ERR_INVALID_ARG, None)
     assert sw.swiglu_graph_launch(None, 0) == sw.SWIGLU_ERR_INVALID_ARG
     assert sw.swiglu_graph_destroy(None) == sw.SWIGLU_OK
 

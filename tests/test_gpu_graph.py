@@ -122,3 +122,31 @@ def test_empty_batch_records_an_empty_graph():
         torch_mod().cuda.synchronize()
     finally:
         sw.swiglu_graph_destroy(g)
+
+
+@pytest.mark.parametrize("case", [(16, 1024, 1408, BF16), (130, 264, 712, BF16)])
+def test_block_graph_replays_equal_the_direct_call(case):
+    M, d, dff, dtype = case
+    torch = torch_mod()
+    inp = wl.random_inputs(301 + M, M, d, dff, dtype, with_down=True)
+    wp, wdp = pack(inp, d, dff, dtype)
+    r = dev(inp["x"])
+    gamma = dev(wl.to_storage(1.0 + 0.1 * wl.normal(5, (d,), 1.0), dtype))
+    bias = dev(wl.to_storage(wl.normal(6, (d,), 0.1), dtype))
+    nb = sw.mlp_block_workspace_bytes(M, d, dff, dtype)
+    ws = bytes_buf(nb)
+    ref = empty((M, d), dtype)
+    sw.check(sw.mlp_block_forward(r, gamma, 1e-6, wp, wdp, bias, ref, M, d, dff, dtype, ws, nb))
+    torch.cuda.synchronize()
+    out = empty((M, d), dtype)
+    rc, g = sw.mlp_block_graph_create(r, gamma, 1e-6, wp, wdp, bias, out, M, d, dff, dtype, ws, nb)
+    sw.check(rc, "block graph create")
+    try:
+        for _ in range(3):
+            out.fill_(-1)
+            torch.cuda.synchronize()
+            sw.check(sw.swiglu_graph_launch(g))
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref)
+    finally:
+        sw.swiglu_graph_destroy(g)
