@@ -232,6 +232,10 @@ def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0,
                                   if not (path or graph or block) else None)
     res["roofline"]["kernel"] = kern
     res["roofline"]["kernel_ms"] = round(per_launch_ms, 5)
+    if r.path in (2, 3) and not (w.with_down or block or graph):
+        # with the reported workspace the many-rows step packs x first; the
+        # events span both launches
+        res["roofline"]["step_kernels"] = ["pack_act_kernel", kern]
     return res
 
 

@@ -111,30 +111,80 @@ size_t partial_bytes(const GemmArgs& g, int path)
     return skinny_partial_bytes(g, plan_skinny(g, TARGET_CUS));
 }
 
+bool is_wide(int path) { return path == SWIGLU_PATH_WIDE || path == SWIGLU_PATH_WIDE_PHASED; }
+
 size_t h_bytes(int64_t M, int64_t d, int64_t dff, int dt)
 {
     return align_up((size_t)M * (size_t)gateup_geom(d, dff, dt).padded_cols() * elem_bytes(dt));
 }
 
-// Workspace need, or a negative status.
+// Launch plan and workspace regions of one call.  With the full workspace
+// ("packed" mode, when the gate/up product takes the MFMA path) the
+// activations go to that kernel in the packed layout of geometry.h: x is
+// packed into the workspace first (region xp), and h is written packed when
+// the down product also takes the MFMA path.  A workspace of at least the
+// minimum size runs the same kernels on row-major activations instead.
+struct Plan {
+    GemmArgs u, dn;       // the products (dn: with_down only)
+    int pu, pd;           // their paths (pd: with_down only)
+    bool packed;
+    size_t h, xp, part;   // region sizes: h, packed activations, split-K partials
+    size_t need() const { return h + xp + part; }
+};
+
+// Plan for a call, or a negative status in rc.
+Plan make_plan(int64_t M, int64_t d, int64_t dff, int dt, int with_down, int path, bool want_packed,
+               int* rc)
+{
+    Plan p;
+    memset(&p, 0, sizeof p);
+    p.u = up_args(M, d, dff, dt, with_down != 0);
+    p.pu = resolve_path(p.u, path);
+    *rc = p.pu < 0 ? p.pu : SWIGLU_OK;
+    size_t part = p.pu < 0 ? 0 : partial_bytes(p.u, p.pu);
+    if (with_down) {
+        p.dn = down_args(M, d, dff, dt);
+        p.pd = resolve_path(p.dn, path);
+        if (*rc == SWIGLU_OK && p.pd < 0)
+            *rc = p.pd;
+        const size_t pb = p.pd < 0 ? 0 : partial_bytes(p.dn, p.pd);
+        part = part > pb ? part : pb;
+    }
+    if (*rc != SWIGLU_OK)
+        return p;
+    p.packed = want_packed && is_wide(p.pu);
+    p.part = align_up(part);
+    if (p.packed)
+        p.xp = align_up((size_t)act_packed_bytes(M, p.u.geom.nkc));
+    if (with_down)
+        p.h = p.packed && p.pd == SWIGLU_PATH_WIDE
+                  ? align_up((size_t)act_packed_bytes(M, p.dn.geom.nkc))
+                  : h_bytes(M, d, dff, dt);
+    return p;
+}
+
+// The packed plan when the workspace holds it, else the minimum plan, else
+// SWIGLU_ERR_WORKSPACE (also when a workspace is needed and ws is null).
+int choose_plan(int64_t M, int64_t d, int64_t dff, int dt, int with_down, int path, const void* ws,
+                size_t ws_bytes, Plan* out)
+{
+    int rc;
+    for (int packed = 1; packed >= 0; --packed) {
+        *out = make_plan(M, d, dff, dt, with_down, path, packed != 0, &rc);
+        if (rc != SWIGLU_OK)
+            return rc;
+        if (out->need() <= ws_bytes && (out->need() == 0 || ws))
+            return SWIGLU_OK;
+    }
+    return SWIGLU_ERR_WORKSPACE;
+}
+
+// Workspace size that enables the packed plan, or a negative status.
 int64_t workspace_need(int64_t M, int64_t d, int64_t dff, int dt, int with_down, int path)
 {
-    if (!with_down) {
-        GemmArgs u = up_args(M, d, dff, dt, false);
-        int pu = resolve_path(u, path);
-        if (pu < 0)
-            return pu;
-        return (int64_t)align_up(partial_bytes(u, pu));
-    }
-    GemmArgs u = up_args(M, d, dff, dt, true);
-    GemmArgs dn = down_args(M, d, dff, dt);
-    int pu = resolve_path(u, path), pd = resolve_path(dn, path);
-    if (pu < 0)
-        return pu;
-    if (pd < 0)
-        return pd;
-    size_t pa = partial_bytes(u, pu), pb = partial_bytes(dn, pd);
-    return (int64_t)(h_bytes(M, d, dff, dt) + align_up(pa > pb ? pa : pb));
+    int rc;
+    const Plan p = make_plan(M, d, dff, dt, with_down, path, true, &rc);
+    return rc != SWIGLU_OK ? rc : (int64_t)p.need();
 }
 
 int run(const GemmArgs& g, int path, void* partial, hipStream_t s)
@@ -147,6 +197,25 @@ int run(const GemmArgs& g, int path, void* partial, hipStream_t s)
     else
         e = launch_skinny(g, plan_skinny(g, TARGET_CUS), (float*)partial, s);
     return e == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_HIP;
+}
+
+// The gate/up product of a plan on activations x (row-major, or already
+// packed when x_packed), writing out; in the packed plan a row-major x is
+// packed into xp first.
+int run_up(GemmArgs u, int pu, bool packed, const void* x, bool x_packed, void* xp, void* out,
+           void* partial, hipStream_t s)
+{
+    u.a = x;
+    if (packed) {
+        if (!x_packed) {
+            if (launch_pack_act(x, u.lda, u.M, u.geom.K, u.geom.nkc, xp, s) != hipSuccess)
+                return SWIGLU_ERR_HIP;
+            u.a = xp;
+        }
+        u.a_packed = 1;
+    }
+    u.out = out;
+    return run(u, pu, partial, s);
 }
 
 // do_up / do_mlp check every argument, then launch unless `launch` is
@@ -163,47 +232,35 @@ int do_up(const void* x, const void* wp, void* out, int64_t M, int64_t d, int64_
         return SWIGLU_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(wp) || !aligned16(out) || (ws && !aligned16(ws)))
         return SWIGLU_ERR_MISALIGNED;
-    GemmArgs g = up_args(M, d, dff, dtype, false);
-    int p = resolve_path(g, path);
-    if (p < 0)
-        return p;
-    int64_t need = workspace_need(M, d, dff, dtype, 0, path);
-    if (need < 0)
-        return (int)need;
-    if ((size_t)need > ws_bytes || (need > 0 && !ws))
-        return SWIGLU_ERR_WORKSPACE;
-    if (!launch)
-        return SWIGLU_OK;
-    g.a = x;
-    g.w = wp;
-    g.out = out;
-    return run(g, p, ws, s);
+    Plan p;
+    rc = choose_plan(M, d, dff, dtype, 0, path, ws, ws_bytes, &p);
+    if (rc != SWIGLU_OK || !launch)
+        return rc;
+    p.u.w = wp;
+    uint8_t* xp = (uint8_t*)ws;
+    return run_up(p.u, p.pu, p.packed, x, false, xp, out, xp + p.xp, s);
 }
 
-// Launches of the MLP on checked arguments: h = silu(x.Wg) * (x.Wu) into
-// the workspace, then y = h.Wd (+ bias) (+ resid).
-int run_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, int64_t d,
-            int64_t dff, int dtype, void* ws, hipStream_t s, int path, const void* resid,
-            const void* bias)
+// Launches of the MLP on a checked plan: h = silu(x.Wg) * (x.Wu) into the
+// workspace, then y = h.Wd (+ bias) (+ resid).
+int run_mlp(Plan p, const void* x, bool x_packed, const void* wp, const void* wdp, void* y,
+            void* h, void* xp, void* partial, hipStream_t s, const void* resid, const void* bias)
 {
-    GemmArgs u = up_args(M, d, dff, dtype, true);
-    GemmArgs dn = down_args(M, d, dff, dtype);
-    const int pu = resolve_path(u, path), pd = resolve_path(dn, path);
-    uint8_t* h = (uint8_t*)ws;
-    uint8_t* partial = h + h_bytes(M, d, dff, dtype);
-    u.a = x;
-    u.w = wp;
-    u.out = h;
-    int rc = run(u, pu, partial, s);
+    p.u.w = wp;
+    const bool h_packed = p.packed && p.pd == SWIGLU_PATH_WIDE;
+    if (h_packed)
+        p.u.out_nkc = p.dn.geom.nkc;
+    int rc = run_up(p.u, p.pu, p.packed, x, x_packed, xp, h, partial, s);
     if (rc != SWIGLU_OK)
         return rc;
-    dn.a = h;
-    dn.w = wdp;
-    dn.out = y;
-    dn.resid = resid;
-    dn.ldr = d;
-    dn.bias = bias;
-    return run(dn, pd, partial, s);
+    p.dn.a = h;
+    p.dn.a_packed = h_packed;
+    p.dn.w = wdp;
+    p.dn.out = y;
+    p.dn.resid = resid;
+    p.dn.ldr = p.dn.ldo;
+    p.dn.bias = bias;
+    return run(p.dn, p.pd, partial, s);
 }
 
 int do_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, int64_t d,
@@ -219,31 +276,43 @@ int do_mlp(const void* x, const void* wp, const void* wdp, void* y, int64_t M, i
         return SWIGLU_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(wp) || !aligned16(wdp) || !aligned16(y) || !aligned16(ws))
         return SWIGLU_ERR_MISALIGNED;
-    GemmArgs u = up_args(M, d, dff, dtype, true);
-    GemmArgs dn = down_args(M, d, dff, dtype);
-    int pu = resolve_path(u, path), pd = resolve_path(dn, path);
-    if (pu < 0)
-        return pu;
-    if (pd < 0)
-        return pd;
-    int64_t need = workspace_need(M, d, dff, dtype, 1, path);
-    if (need < 0)
-        return (int)need;
-    if ((size_t)need > ws_bytes)
-        return SWIGLU_ERR_WORKSPACE;
-    if (!launch)
-        return SWIGLU_OK;
-    return run_mlp(x, wp, wdp, y, M, d, dff, dtype, ws, s, path, nullptr, nullptr);
+    Plan p;
+    rc = choose_plan(M, d, dff, dtype, 1, path, ws, ws_bytes, &p);
+    if (rc != SWIGLU_OK || !launch)
+        return rc;
+    uint8_t* h = (uint8_t*)ws;
+    return run_mlp(p, x, false, wp, wdp, y, h, h + p.h, h + p.h + p.xp, s, nullptr, nullptr);
 }
 
 // The MLP block: out = r + MLP(rmsnorm(r)) (+ bias).  Workspace: the
-// normalised rows n (M x d, activation type), then the MLP's workspace.
+// normalised rows n, then h and the partials.  In the packed plan RMSNorm
+// writes n directly in the packed layout (n takes the place of xp).
 size_t n_bytes(int64_t M, int64_t d, int dt) { return align_up((size_t)M * d * elem_bytes(dt)); }
 
-int64_t block_need(int64_t M, int64_t d, int64_t dff, int dt, int path)
+size_t block_need(const Plan& p, int64_t M, int64_t d, int dt)
 {
-    const int64_t mlp = workspace_need(M, d, dff, dt, 1, path);
-    return mlp < 0 ? mlp : (int64_t)n_bytes(M, d, dt) + mlp;
+    return p.packed ? p.need() : n_bytes(M, d, dt) + p.need();
+}
+
+int choose_block_plan(int64_t M, int64_t d, int64_t dff, int dt, int path, size_t ws_bytes,
+                      Plan* out)
+{
+    int rc;
+    for (int packed = 1; packed >= 0; --packed) {
+        *out = make_plan(M, d, dff, dt, 1, path, packed != 0, &rc);
+        if (rc != SWIGLU_OK)
+            return rc;
+        if (block_need(*out, M, d, dt) <= ws_bytes)
+            return SWIGLU_OK;
+    }
+    return SWIGLU_ERR_WORKSPACE;
+}
+
+int64_t block_workspace_need(int64_t M, int64_t d, int64_t dff, int dt, int path)
+{
+    int rc;
+    const Plan p = make_plan(M, d, dff, dt, 1, path, true, &rc);
+    return rc != SWIGLU_OK ? rc : (int64_t)block_need(p, M, d, dt);
 }
 
 int do_block(const void* r, const void* gamma, float eps, const void* wp, const void* wdp,
@@ -260,23 +329,17 @@ int do_block(const void* r, const void* gamma, float eps, const void* wp, const 
     if (!aligned16(r) || !aligned16(gamma) || !aligned16(wp) || !aligned16(wdp) ||
         !aligned16(out) || !aligned16(ws) || ((uintptr_t)bias % elem_bytes(dtype)) != 0)
         return SWIGLU_ERR_MISALIGNED;
-    GemmArgs u = up_args(M, d, dff, dtype, true);
-    GemmArgs dn = down_args(M, d, dff, dtype);
-    if (resolve_path(u, path) < 0)
-        return resolve_path(u, path);
-    if (resolve_path(dn, path) < 0)
-        return resolve_path(dn, path);
-    const int64_t need = block_need(M, d, dff, dtype, path);
-    if (need < 0)
-        return (int)need;
-    if ((size_t)need > ws_bytes)
-        return SWIGLU_ERR_WORKSPACE;
-    if (!launch)
-        return SWIGLU_OK;
+    Plan p;
+    rc = choose_block_plan(M, d, dff, dtype, path, ws_bytes, &p);
+    if (rc != SWIGLU_OK || !launch)
+        return rc;
     uint8_t* n = (uint8_t*)ws;
-    if (launch_rmsnorm(r, gamma, eps, M, d, dtype, n, s) != hipSuccess)
+    const size_t nb = p.packed ? p.xp : n_bytes(M, d, dtype);
+    if (launch_rmsnorm(r, gamma, eps, M, d, dtype, n, p.packed ? p.u.geom.nkc : 0, s) !=
+        hipSuccess)
         return SWIGLU_ERR_HIP;
-    return run_mlp(n, wp, wdp, out, M, d, dff, dtype, n + n_bytes(M, d, dtype), s, path, r, bias);
+    uint8_t* h = n + nb;
+    return run_mlp(p, n, p.packed, wp, wdp, out, h, nullptr, h + p.h, s, r, bias);
 }
 
 // Records one call (`call(stream, launch)` returns a status) on a private
@@ -450,7 +513,7 @@ size_t mlp_block_workspace_bytes_ex(int64_t M, int64_t d, int64_t dff, int dtype
 {
     if (check_sizes(M, d, dff, dtype) != SWIGLU_OK || check_path(path) != SWIGLU_OK || M == 0)
         return 0;
-    const int64_t need = block_need(M, d, dff, dtype, path);
+    const int64_t need = block_workspace_need(M, d, dff, dtype, path);
     return need < 0 ? 0 : (size_t)need;
 }
 

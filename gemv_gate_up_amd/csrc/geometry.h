@@ -102,6 +102,22 @@ __host__ __device__ inline PackGeom gateup_geom(int64_t d, int64_t dff, int dt) 
     return g;
 }
 
+// Packed activations (bf16, many-rows path).  The left operand of the MFMA
+// GEMM, M x K, laid out as its A fragments: pieces ordered [row block of 16]
+// [32-K chunk], and lane l of a piece holding row l % 16 and the 8
+// consecutive K values of k-group l / 16 of its chunk, i.e. element (row, k)
+// at index ((row / 16) * nkc + k / 32) * 512 + ((k % 32) / 8 * 16 + row % 16)
+// * 8 + k % 8.  Rows are padded to a multiple of 16 and K to the nkc chunks
+// of the weight that consumes it; padding is zero.  A piece is one
+// contiguous 1 KB load, where a row-major tile row is a 64-byte fragment of
+// a line per K step.
+__host__ __device__ inline int64_t act_packed_bytes(int64_t M, int64_t nkc) {
+    return ceil_div(M, 16) * nkc * PIECE_BYTES;
+}
+__host__ __device__ inline int64_t act_packed_index(int64_t row, int64_t k, int64_t nkc) {
+    return ((row / 16) * nkc + k / 32) * 512 + ((k % 32) / 8 * 16 + row % 16) * 8 + k % 8;
+}
+
 // Down weight: contraction over dff, d output columns.
 __host__ __device__ inline PackGeom down_geom(int64_t d, int64_t dff, int dt) {
     PackGeom g;

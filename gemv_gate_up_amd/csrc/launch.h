@@ -16,10 +16,13 @@ hipError_t launch_pack(const void* src0, const void* src1, void* dst, const Pack
 struct GemmArgs {
     const void* a;      // activations, M x lda row-major (x, or h in the workspace)
     int64_t lda;        // row stride of a in elements
+    int a_packed;       // wide path: a is in the packed activation layout (lda unused)
     const void* w;      // packed weights
     PackGeom geom;      // geometry of w
     void* out;          // output, M x ldo row-major
     int64_t ldo;        // row stride of out in elements
+    int64_t out_nkc;    // > 0, wide path: out is written in the packed activation layout
+                        // with this many 32-K chunks (ldo unused); see geometry.h
     int64_t ncols_out;  // output columns to store (valid columns, or the padded width)
     int64_t M;
     int epi;            // EPI_SWIGLU or EPI_PLAIN
@@ -30,10 +33,16 @@ struct GemmArgs {
     const void* bias;   // ncols_out values, activation type
 };
 
+// Packs M x K bf16 activations (row stride lda) into the packed activation
+// layout with nkc chunks (pack.hip).
+hipError_t launch_pack_act(const void* x, int64_t lda, int64_t M, int64_t K, int64_t nkc, void* dst,
+                           hipStream_t s);
+
 // RMSNorm prologue (norm.hip): n = r / sqrt(mean(r^2) + eps) * gamma per
-// row; r, gamma and n in the activation type of dt.
+// row; r, gamma and n in the activation type of dt.  packed_nkc > 0 (bf16
+// only): n is written in the packed activation layout with that many chunks.
 hipError_t launch_rmsnorm(const void* r, const void* gamma, float eps, int64_t M, int64_t d,
-                          int dt, void* n, hipStream_t s);
+                          int dt, void* n, int64_t packed_nkc, hipStream_t s);
 
 // Split-K plan for the skinny kernels.
 struct SkinnyPlan {

@@ -9,7 +9,10 @@
 // in each wave and then in wave order, so the result does not depend on
 // timing.  1 / sqrt uses correctly rounded fp32 square root and division.
 // The normalised row is rounded once to the activation type (bf16 or fp32)
-// and feeds the gate/up product.
+// and feeds the gate/up product: row-major, or (bf16, for the many-rows
+// path) directly in the packed activation layout of geometry.h, in which
+// case the grid also covers the padding rows and each workgroup writes the
+// zero K padding of its row.
 #include "device_common.h"
 #include "launch.h"
 
@@ -19,14 +22,22 @@ constexpr int NORM_THREADS = 256;
 
 template <typename T>
 __global__ void __launch_bounds__(NORM_THREADS)
-rmsnorm_kernel(const T* __restrict__ r, const T* __restrict__ gamma, float eps, int64_t d,
-               T* __restrict__ n)
+rmsnorm_kernel(const T* __restrict__ r, const T* __restrict__ gamma, float eps, int64_t M,
+               int64_t d, T* __restrict__ n, int64_t packed_nkc)
 {
     constexpr int VE = 16 / sizeof(T);
     const int64_t row = blockIdx.x;
-    const T* rr = r + row * d;
-    T* nr = n + row * d;
     const int64_t nvec = d / VE;
+    // destination of vector v (elements v*VE ..) of this row
+    auto dst = [&](int64_t v) {
+        return packed_nkc > 0 ? n + act_packed_index(row, v * VE, packed_nkc) : n + row * d + v * VE;
+    };
+    if (row >= M) {   // padding row of the packed layout
+        for (int64_t v = threadIdx.x; v < packed_nkc * 32 / VE; v += NORM_THREADS)
+            *(i32x4*)dst(v) = i32x4{0, 0, 0, 0};
+        return;
+    }
+    const T* rr = r + row * d;
     float ss = 0.f;
     for (int64_t v = threadIdx.x; v < nvec; v += NORM_THREADS) {
         const i32x4 raw = *(const i32x4*)(rr + v * VE);
@@ -59,19 +70,25 @@ rmsnorm_kernel(const T* __restrict__ r, const T* __restrict__ gamma, float eps, 
 #pragma unroll
         for (int k = 0; k < VE; ++k)
             store_out(oe + k, load_act(e + k) * inv * load_act(g + k));
-        *(i32x4*)(nr + v * VE) = o;
+        *(i32x4*)dst(v) = o;
     }
+    for (int64_t v = nvec + threadIdx.x; v < packed_nkc * 32 / VE; v += NORM_THREADS)
+        *(i32x4*)dst(v) = i32x4{0, 0, 0, 0};
 }
 
 hipError_t launch_rmsnorm(const void* r, const void* gamma, float eps, int64_t M, int64_t d,
-                          int dt, void* n, hipStream_t s)
+                          int dt, void* n, int64_t packed_nkc, hipStream_t s)
 {
-    if (dt == DT_F32)
+    if (dt == DT_F32) {
+        if (packed_nkc > 0)
+            return hipErrorInvalidValue;
         rmsnorm_kernel<float><<<dim3((unsigned)M), dim3(NORM_THREADS), 0, s>>>(
-            (const float*)r, (const float*)gamma, eps, d, (float*)n);
-    else
-        rmsnorm_kernel<uint16_t><<<dim3((unsigned)M), dim3(NORM_THREADS), 0, s>>>(
-            (const uint16_t*)r, (const uint16_t*)gamma, eps, d, (uint16_t*)n);
+            (const float*)r, (const float*)gamma, eps, M, d, (float*)n, 0);
+    } else {
+        const int64_t rows = packed_nkc > 0 ? round_up(M, 16) : M;
+        rmsnorm_kernel<uint16_t><<<dim3((unsigned)rows), dim3(NORM_THREADS), 0, s>>>(
+            (const uint16_t*)r, (const uint16_t*)gamma, eps, M, d, (uint16_t*)n, packed_nkc);
+    }
     return hipGetLastError();
 }
 

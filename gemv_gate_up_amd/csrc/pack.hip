@@ -207,6 +207,39 @@ pack_mxfp4_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict_
     dst[v] = i32x4{(int)word[0], (int)word[1], (int)word[2], (int)word[3]};
 }
 
+// Activations into the packed layout of geometry.h, one thread per 16-byte
+// vector of the output: the 64 threads of a piece read 16 rows x 64
+// contiguous bytes and write the piece as one 1 KB run.  Vectors of padded
+// rows or K are zero.  K is a multiple of 8, so a vector is all valid or all
+// padding.
+__global__ void __launch_bounds__(256)
+pack_act_kernel(const uint16_t* __restrict__ x, int64_t lda, int64_t M, int64_t K, int64_t nkc,
+                uint16_t* __restrict__ dst, int64_t total_vecs)
+{
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= total_vecs)
+        return;
+    const int lane = (int)(v % PIECE_VECS);
+    const int64_t piece = v / PIECE_VECS;
+    const int64_t row = (piece / nkc) * 16 + lane % 16;
+    const int64_t k = (piece % nkc) * 32 + (lane / 16) * 8;
+    i32x4 val = {0, 0, 0, 0};
+    if (row < M && k < K)
+        val = *(const i32x4*)(x + row * lda + k);
+    *(i32x4*)(dst + v * 8) = val;
+}
+
+hipError_t launch_pack_act(const void* x, int64_t lda, int64_t M, int64_t K, int64_t nkc, void* dst,
+                           hipStream_t s)
+{
+    const int64_t total = act_packed_bytes(M, nkc) / 16;
+    if (total == 0)
+        return hipSuccess;
+    pack_act_kernel<<<dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s>>>(
+        (const uint16_t*)x, lda, M, K, nkc, (uint16_t*)dst, total);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const void* src0, const void* src1, void* dst, const PackGeom& g,
                        int plain, hipStream_t s)
 {

@@ -132,10 +132,19 @@ size_t swiglu_packed_bytes(int64_t d, int64_t dff, int dtype);
 size_t swiglu_down_packed_bytes(int64_t d, int64_t dff, int dtype);
 
 /*
- * Workspace bytes a call with these sizes needs (0 if none), for
- * swiglu_up (with_down = 0) or mlp_forward (with_down = 1) on the automatic
- * path; the _ex variant gives the size for a forced path.  Returns 0 for
- * invalid arguments as well, which the calls then reject.
+ * Workspace bytes for swiglu_up (with_down = 0) or mlp_forward
+ * (with_down = 1) with these sizes on the automatic path (0 if none); the
+ * _ex variant gives the size for a forced path.  Returns 0 for invalid
+ * arguments as well, which the calls then reject.
+ *
+ * With this much workspace the many-rows (MFMA) path first copies x into
+ * the workspace in the layout of its A operand fragments (row blocks of 16,
+ * K chunks of 32; about M x d x 2 bytes), and mlp_forward keeps h in that
+ * layout, which makes the matrix product faster.  A smaller workspace that
+ * still holds the row-major plan (nothing for swiglu_up on that path; h as
+ * M x padded-dff row-major for mlp_forward) runs the same kernels on x in
+ * place, with bit-identical results.  Below that the call returns
+ * SWIGLU_ERR_WORKSPACE.  The skinny path needs only its split-K partials.
  */
 size_t swiglu_workspace_bytes(int64_t M, int64_t d, int64_t dff, int dtype, int with_down);
 size_t swiglu_workspace_bytes_ex(int64_t M, int64_t d, int64_t dff, int dtype, int with_down,
@@ -168,7 +177,8 @@ int swiglu_pack_down(const void *Wdown, void *Wdpacked, int64_t d, int64_t dff, 
  * from swiglu_pack_weights.  Accumulation in fp32; silu and the product in
  * fp32; one rounding to the output dtype at the store.  workspace (device,
  * may be NULL when swiglu_workspace_bytes returns 0) holds split-K partial
- * sums on the skinny path.
+ * sums on the skinny path and the packed copy of x on the many-rows path
+ * (see swiglu_workspace_bytes).
  */
 int swiglu_up(const void *x, const void *Wpacked, void *out,
               int64_t M, int64_t d, int64_t dff, int dtype,

@@ -108,9 +108,14 @@ def test_forced_paths():
     assert rc == sw.SWIGLU_ERR_UNSUPPORTED
     rc = sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, BF16, None, 0, 0, 4)
     assert rc == sw.SWIGLU_ERR_UNSUPPORTED
-    # the two-pass schedule needs no workspace, with or without the down product
-    assert sw.swiglu_workspace_bytes_ex(4096, 4096, 14336, BF16, 0,
-                                        sw.SWIGLU_PATH_WIDE_PHASED) == 0
+    # both many-rows schedules take x packed into the workspace: one 1 KB
+    # piece per 16 rows x 32 K (they also run without it, on x in place)
+    packed_x = (4096 // 16) * (4096 // 32) * 1024
+    for path in (sw.SWIGLU_PATH_WIDE, sw.SWIGLU_PATH_WIDE_PHASED, sw.SWIGLU_PATH_AUTO):
+        assert sw.swiglu_workspace_bytes_ex(4096, 4096, 14336, BF16, 0, path) == packed_x
+    # rows padded to 16, K to the weight's 64
+    assert sw.swiglu_workspace_bytes_ex(130, 264, 712, BF16, 0, sw.SWIGLU_PATH_WIDE) == \
+        9 * 10 * 1024
     assert sw.swiglu_workspace_bytes_ex(96, 512, 1408, BF16, 1, sw.SWIGLU_PATH_WIDE_PHASED) == \
         sw.swiglu_workspace_bytes_ex(96, 512, 1408, BF16, 1, sw.SWIGLU_PATH_WIDE)
 
@@ -176,6 +181,10 @@ def test_mlp_block_arguments_and_workspace():
     need = sw.mlp_block_workspace_bytes(M, d, dff, BF16)
     # the normalised rows come first, then the MLP's own workspace
     assert need == 256 * -(-(M * d * 2) // 256) + sw.swiglu_workspace_bytes(M, d, dff, BF16, 1)
+    # on the many-rows path RMSNorm writes its rows already packed, in the
+    # place the MLP would pack x into
+    assert sw.mlp_block_workspace_bytes(4096, 4096, 14336, BF16) == \
+        sw.swiglu_workspace_bytes(4096, 4096, 14336, BF16, 1)
     blk = lambda *a, **k: sw.mlp_block_forward(*a, stream=0, **k)
     assert blk(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, 0, d, dff, BF16) == sw.SWIGLU_OK
     assert blk(FAKE, FAKE, -1.0, FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE,
