@@ -352,61 +352,63 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     }
 
     // ---- epilogue: lane l holds rows 4*(l/16)+i of column l%16 of each
-    // fragment.  The finished values (silu(gate) * up, or the plain
-    // product) are staged in LDS one wave-row of the tile at a time, then
-    // written to memory as whole rows in 16-byte vectors, so every global
-    // write covers full cache lines.
+    // fragment.  Every wave first turns its accumulators into the finished
+    // bf16 values in registers (silu(gate) * up, or the plain product with
+    // bias and residual), all waves at once; the values are then staged in
+    // LDS (the ring is free by now) as many wave-rows at a time as fit (the
+    // whole tile for the gate/up product) and written to memory as whole
+    // rows of 16-byte vectors, so every global write covers full lines.
     constexpr int OW = EPI == EPI_SWIGLU && !PHASED ? BN / 2 : BN;   // output columns of the tile
     constexpr int WOW = OW / WGN;                          // of one wave
+    constexpr int FO = WOW / 16;                           // output fragments across a wave
     constexpr int LROW = OW + 8;                           // padded LDS row, elements
     constexpr int VPR = OW / 8;                            // 16-byte vectors per row
-    static_assert(S::WTM * LROW * 2 <= S::LDS_BYTES, "epilogue staging fits the ring");
+    constexpr int WR_FIT = S::LDS_BYTES / (S::WTM * LROW * 2);
+    constexpr int WRP = WR_FIT >= WGM ? WGM : (WR_FIT >= WGM / 2 ? WGM / 2 : 1);   // wave-rows per pass
+    constexpr int PROWS = WRP * S::WTM;                    // tile rows per pass
+    static_assert(WRP >= 1 && WGM % WRP == 0 && PROWS * LROW * 2 <= S::LDS_BYTES,
+                  "epilogue staging fits the ring");
     uint16_t* ep = (uint16_t*)smem;
     const int64_t col0 = EPI == EPI_SWIGLU ? pb0 * 16 : pb0 * 32;
     (void)gs;
     const int c = lane & 15;
-#pragma unroll 1
-    for (int pass = 0; pass < WGM; ++pass) {
-        __syncthreads();   // ring reads (first pass) or previous stores (later) are done
-        if (wm == pass) {
+    // fragment j of the wave holds output column wn * WOW + 16 * j + c
+    uint16_t res[FM][FO][4];
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int j = 0; j < FO; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v;
                 if constexpr (PHASED) {
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = fm * 16 + (lane >> 4) * 4 + i;
-                            ep[r * LROW + wn * WOW + fn * 16 + c] =
-                                f32_to_bf16(gs[fm][fn][i] * acc[fm][fn][i]);
-                        }
-                    continue;
+                    v = gs[fm][j][i] * acc[fm][j][i];
+                } else if constexpr (EPI == EPI_SWIGLU) {
+                    v = silu(acc[fm][2 * j][i]) * acc[fm][2 * j + 1][i];
+                } else {
+                    v = acc[fm][j][i];
+                    // bias and residual only inside the output
+                    const int64_t grow = m0 + wm * S::WTM + fm * 16 + (lane >> 4) * 4 + i;
+                    const int64_t gcol = col0 + wn * WOW + 16 * j + c;
+                    if ((resid || bias) && grow < M && gcol < ncols_out)
+                        v = plain_tail(v, resid, ldr, bias, grow, gcol);
                 }
+                res[fm][j][i] = f32_to_bf16(v);
+            }
+#pragma unroll 1
+    for (int pass = 0; pass < WGM / WRP; ++pass) {
+        __syncthreads();   // ring reads (first pass) or previous stores (later) are done
+        if (wm / WRP == pass) {
+            const int rbase = (wm % WRP) * S::WTM;
 #pragma unroll
-                for (int jp = 0; jp < FN / 2; ++jp) {
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int j = 0; j < FO; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int r = fm * 16 + (lane >> 4) * 4 + i;
-                        if (EPI == EPI_SWIGLU) {
-                            const float v = silu(acc[fm][2 * jp][i]) * acc[fm][2 * jp + 1][i];
-                            ep[r * LROW + wn * WOW + jp * 16 + c] = f32_to_bf16(v);
-                        } else {
-                            const int cc = wn * WOW + jp * 32 + c;
-                            float v0 = acc[fm][2 * jp][i], v1 = acc[fm][2 * jp + 1][i];
-                            // bias and residual only inside the output
-                            const int64_t grow = m0 + pass * S::WTM + r, gcol = col0 + cc;
-                            if ((resid || bias) && grow < M) {
-                                if (gcol < ncols_out)
-                                    v0 = plain_tail(v0, resid, ldr, bias, grow, gcol);
-                                if (gcol + 16 < ncols_out)
-                                    v1 = plain_tail(v1, resid, ldr, bias, grow, gcol + 16);
-                            }
-                            ep[r * LROW + cc] = f32_to_bf16(v0);
-                            ep[r * LROW + cc + 16] = f32_to_bf16(v1);
-                        }
+                        const int r = rbase + fm * 16 + (lane >> 4) * 4 + i;
+                        ep[r * LROW + wn * WOW + 16 * j + c] = res[fm][j][i];
                     }
-                }
-            }
         }
         __syncthreads();
         if constexpr (PO) {
@@ -414,21 +416,21 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
             // (the padded rows hold the zero products of zero rows) and
             // chunks up to out_nkc
             constexpr int CPR = OW / 32;   // chunks across the tile
-            static_assert(S::WTM % 16 == 0 && OW % 32 == 0, "whole pieces per pass");
+            static_assert(PROWS % 16 == 0 && OW % 32 == 0, "whole pieces per pass");
             const int64_t rows_pad = round_up(M, 16);
-            for (int v = threadIdx.x; v < S::WTM * VPR; v += S::THREADS) {
+            for (int v = threadIdx.x; v < PROWS * VPR; v += S::THREADS) {
                 const int l = v & 63, p = v >> 6;
                 const int r = (p / CPR) * 16 + (l & 15), ch = p % CPR, kg = l >> 4;
-                const int64_t row = m0 + pass * S::WTM + r;
+                const int64_t row = m0 + pass * PROWS + r;
                 const int64_t col = col0 + ch * 32 + kg * 8;
                 if (row < rows_pad && col < out_nkc * 32)
                     *(i32x4*)(out + act_packed_index(row, col, out_nkc)) =
                         *(const i32x4*)(ep + r * LROW + ch * 32 + kg * 8);
             }
         } else {
-            for (int v = threadIdx.x; v < S::WTM * VPR; v += S::THREADS) {
+            for (int v = threadIdx.x; v < PROWS * VPR; v += S::THREADS) {
                 const int r = v / VPR, cv = v % VPR;
-                const int row = m0 + pass * S::WTM + r;
+                const int row = m0 + pass * PROWS + r;
                 const int64_t col = col0 + cv * 8;
                 if (row < M && col < ncols_out)
                     *(i32x4*)(out + (int64_t)row * ldo + col) =
