@@ -20,6 +20,23 @@ struct WidePhasedCfg {
 };
 static_assert(WideCfg::BN / 32 == WidePhasedCfg::BN / 16, "both schedules tile 8 pair blocks");
 
+// The last, partial round of 256 x 256 tiles runs as quarter tiles: when
+// the tile count leaves a last round of at most half the compute units
+// (the 72B-class gate/up product: 1,848 tiles = 7 rounds + 56), those
+// tiles are launched separately as 4 x as many 128 x 128 tiles on
+// otherwise idle units.  Those finish in about half (not a quarter) of a
+// full tile's time: a quarter tile's step has a quarter of the matrix work
+// but the same load latency to hide, hence its deeper ring (8 stages of
+// 16 KB).  Measured on the 72B-class gate/up product: the tail round
+// 213 -> about 95 us.  Every output sums the same MFMAs in the same K
+// order, so the results are the same bit for bit.
+struct WideTailCfg {
+    static constexpr int BM = 128, BN = 128, WGM = 4, WGN = 2, KCS = 1, STAGES = 8;
+};
+static_assert(2 * WideTailCfg::BM == WideCfg::BM && 2 * WideTailCfg::BN == WideCfg::BN,
+              "quarter tiles");
+constexpr int WIDE_CUS = 256;   // MI355X compute units: one 256 x 256 tile each per round
+
 int wide_supported(const GemmArgs& g)
 {
     // bf16 only; the A region of one tile must stay under 2 GB of byte
@@ -32,22 +49,45 @@ hipError_t wide_prepare()
 {
     using C = WideCfg;
     using P = WidePhasedCfg;
+    using T = WideTailCfg;
     hipError_t e = wide_attrs<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_SWIGLU>();
     if (e == hipSuccess)
         e = wide_attrs<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_PLAIN>();
+    if (e == hipSuccess)
+        e = wide_attrs<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI_SWIGLU>();
+    if (e == hipSuccess)
+        e = wide_attrs<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI_PLAIN>();
     if (e == hipSuccess)
         e = wide_attrs<P::BM, P::BN, P::WGM, P::WGN, P::KCS, P::STAGES, EPI_SWIGLU, true>();
     return e;
 }
 
-hipError_t launch_wide(const GemmArgs& g, hipStream_t s)
+template <int EPI>
+static hipError_t launch_wide_epi(const GemmArgs& g, hipStream_t s)
 {
     using C = WideCfg;
-    if (g.epi == EPI_SWIGLU)
-        return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_SWIGLU>(
-            g, s, C::GROUP_M);
-    return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_PLAIN>(
-        g, s, C::GROUP_M);
+    using T = WideTailCfg;
+    WideGrid full = wide_full_grid<C::BM, C::BN, C::BN / 32>(g);
+    const int G = full.blocks;
+    const int tail = G > WIDE_CUS ? G % WIDE_CUS : 0;
+    if (tail == 0 || tail > WIDE_CUS / 2)
+        return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI>(
+            g, s, C::GROUP_M, true, &full);
+    WideGrid head = full, rest = full;
+    head.blocks = G - tail;
+    rest.blocks = 4 * tail;
+    rest.tail_base = G - tail;
+    hipError_t e = launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI>(
+        g, s, C::GROUP_M, true, &head);
+    if (e == hipSuccess)
+        e = launch_wide_cfg<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI>(
+            g, s, C::GROUP_M, true, &rest);
+    return e;
+}
+
+hipError_t launch_wide(const GemmArgs& g, hipStream_t s)
+{
+    return g.epi == EPI_SWIGLU ? launch_wide_epi<EPI_SWIGLU>(g, s) : launch_wide_epi<EPI_PLAIN>(g, s);
 }
 
 hipError_t launch_wide_phased(const GemmArgs& g, hipStream_t s)

@@ -115,11 +115,17 @@ struct WideShape {
 
 template <int PPW, int MAXA>
 __device__ __forceinline__ void wait_stage(int ahead) {
-    // wait until at most `ahead` later stages of this wave remain in flight
-    if (MAXA >= 3 && ahead >= 3) { wait_vmcnt<(MAXA >= 3 ? 3 : 0) * PPW>(); return; }
-    if (MAXA >= 2 && ahead >= 2) { wait_vmcnt<(MAXA >= 2 ? 2 : 0) * PPW>(); return; }
-    if (MAXA >= 1 && ahead >= 1) { wait_vmcnt<PPW>(); return; }
-    wait_vmcnt<0>();
+    // wait until at most min(ahead, MAXA) later stages of this wave remain
+    // in flight
+    if constexpr (MAXA > 0) {
+        if (ahead >= MAXA) {
+            wait_vmcnt<MAXA * PPW>();
+            return;
+        }
+        wait_stage<PPW, MAXA - 1>(ahead);
+    } else {
+        wait_vmcnt<0>();
+    }
 }
 
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED,
@@ -128,7 +134,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64, 1)
 wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, int M,
                  const uint16_t* __restrict__ w, int64_t nkc, int64_t npb,
                  uint16_t* __restrict__ out, int64_t ldo, int64_t ncols_out, int64_t out_nkc,
-                 int tiles_m, int tiles_n, int group_m,
+                 int tiles_m, int tiles_n, int group_m, int tail_base,
                  const uint16_t* __restrict__ resid, int64_t ldr, const uint16_t* __restrict__ bias)
 {
     using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
@@ -144,8 +150,12 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    // ---- tile coordinates: XCD-contiguous ranges, then grouped raster
-    int pid = blockIdx.x;
+    // ---- tile coordinates: XCD-contiguous ranges, then grouped raster over
+    // a grid of tiles_m x tiles_n tiles.  A tail launch (tail_base >= 0)
+    // covers that grid's tiles from tail_base on, each as four quarter tiles
+    // of this kernel's BM x BN (the grid's tiles are 2 BM x 2 BN).
+    const bool tail = tail_base >= 0;
+    int pid = tail ? tail_base + (int)(blockIdx.x >> 2) : (int)blockIdx.x;
     const int G = tiles_m * tiles_n;
     const int per_xcd = G / 8;
     if (pid < per_xcd * 8)
@@ -156,8 +166,11 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     const int tm = first_m + (pid % in_group) % gsz;
     const int tn = (pid % in_group) / gsz;
 
-    const int m0 = tm * BM;
-    const int64_t pb0 = (int64_t)tn * S::PB_TILE;
+    const int sub = tail ? (int)(blockIdx.x & 3) : 0;
+    const int m0 = tail ? tm * 2 * BM + (sub >> 1) * BM : tm * BM;
+    const int64_t pb0 = (tail ? (int64_t)tn * 2 + (sub & 1) : (int64_t)tn) * S::PB_TILE;
+    if (m0 >= M || pb0 >= npb)   // a quarter tile past the output (whole workgroup)
+        return;
     const int rows_here = M - m0 < BM ? M - m0 : BM;
     // packed: the tile's row blocks, [row block][chunk] pieces of 1 KB
     const i32x4 ra =
@@ -455,22 +468,42 @@ static hipError_t wide_attr()
     return e;
 }
 
+// Which tiles one launch covers: the first `blocks` tiles of a tiles_m x
+// tiles_n grid of BM x BN tiles, or (tail_base >= 0) the tiles from
+// tail_base on of a grid of 2 BM x 2 BN tiles, as 4 * blocks quarter tiles.
+struct WideGrid {
+    int tiles_m, tiles_n, blocks, tail_base;
+};
+
+template <int BM, int BN, int PB_TILE>
+WideGrid wide_full_grid(const GemmArgs& g)
+{
+    WideGrid r;
+    r.tiles_m = (int)ceil_div(g.M, BM);
+    r.tiles_n = (int)ceil_div(ceil_div(g.ncols_out, g.geom.cols_per_pb), PB_TILE);
+    r.blocks = r.tiles_m * r.tiles_n;
+    r.tail_base = -1;
+    return r;
+}
+
 // Host launcher for one instantiation.
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED,
           bool PA, bool PO>
-static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m, bool launch)
+static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m, bool launch,
+                                   const WideGrid* grid)
 {
     using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
     const hipError_t e = wide_attr<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED, PA, PO>();
     if (e != hipSuccess || !launch)
         return e;
-    const int tiles_m = (int)ceil_div(g.M, BM);
-    const int tiles_n = (int)ceil_div(ceil_div(g.ncols_out, g.geom.cols_per_pb), S::PB_TILE);
+    const WideGrid gr = grid ? *grid : wide_full_grid<BM, BN, S::PB_TILE>(g);
+    if (gr.blocks <= 0)
+        return hipSuccess;
     wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED, PA, PO>
-        <<<dim3((unsigned)(tiles_m * tiles_n)), dim3(S::THREADS), S::LDS_BYTES, s>>>(
+        <<<dim3((unsigned)gr.blocks), dim3(S::THREADS), S::LDS_BYTES, s>>>(
             (const uint16_t*)g.a, g.lda, g.geom.K, (int)g.M, (const uint16_t*)g.w, g.geom.nkc,
-            g.geom.npb, (uint16_t*)g.out, g.ldo, g.ncols_out, g.out_nkc, tiles_m, tiles_n, group_m,
-            (const uint16_t*)g.resid, g.ldr, (const uint16_t*)g.bias);
+            g.geom.npb, (uint16_t*)g.out, g.ldo, g.ncols_out, g.out_nkc, gr.tiles_m, gr.tiles_n,
+            group_m, gr.tail_base, (const uint16_t*)g.resid, g.ldr, (const uint16_t*)g.bias);
     return hipGetLastError();
 }
 
@@ -479,27 +512,30 @@ static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m
 // stages), packed or row-major output.  With launch = false it only sets
 // the launch attribute of that instantiation.
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED, bool PO>
-static hipError_t launch_wide_out(const GemmArgs& g, hipStream_t s, int group_m, bool launch)
+static hipError_t launch_wide_out(const GemmArgs& g, hipStream_t s, int group_m, bool launch,
+                                  const WideGrid* grid)
 {
     if (g.a_packed)
         return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED, true, PO>(
-            g, s, group_m, launch);
+            g, s, group_m, launch, grid);
     if (g.geom.K % (KCS * 32) == 0)
         return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED, false, PO>(
-            g, s, group_m, launch);
+            g, s, group_m, launch, grid);
     return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, true, PHASED, false, PO>(
-        g, s, group_m, launch);
+        g, s, group_m, launch, grid);
 }
 
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED = false>
-hipError_t launch_wide_cfg(const GemmArgs& g, hipStream_t s, int group_m, bool launch = true)
+hipError_t launch_wide_cfg(const GemmArgs& g, hipStream_t s, int group_m, bool launch = true,
+                           const WideGrid* grid = nullptr)
 {
     if constexpr (EPI == EPI_SWIGLU) {
         if (g.out_nkc > 0)
-            return launch_wide_out<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, true>(g, s, group_m,
-                                                                                   launch);
+            return launch_wide_out<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, true>(
+                g, s, group_m, launch, grid);
     }
-    return launch_wide_out<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, false>(g, s, group_m, launch);
+    return launch_wide_out<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, false>(g, s, group_m, launch,
+                                                                            grid);
 }
 
 // Sets the launch attribute of every instantiation of one configuration.
