@@ -18,7 +18,12 @@
 //   * pairing block = MFMA N fragment (16 columns): lane l holds gate and up
 //     of the same output element, so the epilogue needs no lane exchange;
 //   * tiles are remapped so each XCD (own L2) works through a compact group
-//     of tiles that share A row panels and B column panels.
+//     of tiles that share A row panels and B column panels;
+//   * the epilogue finishes every wave's values in registers at once, then
+//     stages the tile through the freed ring and stores whole rows in
+//     16-byte vectors;
+//   * a launch may cover only part of the tile grid: the full rounds, or
+//     (tail_base >= 0) the last partial round as quarter tiles.
 // The down projection runs through the same kernel with a plain epilogue.
 //
 // PA: the left operand is in the packed activation layout of geometry.h, so
