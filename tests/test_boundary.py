@@ -229,3 +229,38 @@ def test_header_is_plain_c_and_links(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "abi_check ok" in r.stdout
+
+
+def _packed_bytes(M, K):
+    """Packed activations: one 1 KB piece per 16 rows x 32 K, K padded to 64."""
+    return -(-M // 16) * (-(-K // 64) * 2) * 1024
+
+
+def _al(n):
+    return -(-n // 256) * 256
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 14336), (2048, 8192, 29568), (130, 264, 712)])
+def test_packed_plan_workspace_formulas(shape):
+    M, d, dff = shape
+    # swiglu_up on the many-rows path: packed x only
+    assert sw.swiglu_workspace_bytes(M, d, dff, BF16, 0) == _al(_packed_bytes(M, d))
+    # mlp_forward: h packed for the down product, then packed x (no split-K partials)
+    assert sw.swiglu_workspace_bytes(M, d, dff, BF16, 1) == \
+        _al(_packed_bytes(M, dff)) + _al(_packed_bytes(M, d))
+    # the block: RMSNorm's packed rows take the place of packed x
+    assert sw.mlp_block_workspace_bytes(M, d, dff, BF16) == \
+        sw.swiglu_workspace_bytes(M, d, dff, BF16, 1)
+
+
+def test_workspace_below_the_row_major_plan_is_rejected():
+    # the row-major plan of mlp_forward keeps h as M x padded-dff bf16; one
+    # allocation unit less than that fails before any launch
+    M, d, dff = 256, 512, 1408
+    row_major = _al(M * (-(-dff // 128) * 128) * 2)
+    assert sw.swiglu_workspace_bytes(M, d, dff, BF16, 1) > row_major
+    rc = sw.mlp_forward(FAKE, FAKE, FAKE, FAKE, M, d, dff, BF16, FAKE, row_major - 256, stream=0)
+    assert rc == sw.SWIGLU_ERR_WORKSPACE
+    blk = sw.mlp_block_forward(FAKE, FAKE, 1e-6, FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE,
+                               _al(M * d * 2) + row_major - 256, stream=0)
+    assert blk == sw.SWIGLU_ERR_WORKSPACE
