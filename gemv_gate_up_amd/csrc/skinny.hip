@@ -484,9 +484,13 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
         if constexpr (WF == WF_MXFP4) {
             // one piece in flight per half; above 8 rows, four pair blocks
             // per wave when that still leaves a workgroup per CU (measured
-            // at 1, 8 and 16 rows on the 8B and 72B shapes)
+            // at 1, 8 and 16 rows on the 8B and 72B shapes); up to 4 rows,
+            // eight waves per workgroup (8B decode at one row 14.1 -> 13.3
+            // us, 72B 45.0 -> 44.0 us; slower at 8 rows on the 8B shape)
             if (g.M > 8 && p.grid_pb >= 4 * MXFP4_WIDE_PB_CUS)
                 pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
+            else if (g.M <= 4)
+                pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else
                 pick_split_bf16<1, 1, 2, EPI, WF>(g, p, partial, s);
         } else if constexpr (Q) {
