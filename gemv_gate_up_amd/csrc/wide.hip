@@ -5,7 +5,13 @@
 namespace swg {
 
 // 256 x 256 fused-column tile, 8 waves (2 per SIMD) of 64 x 128, stages of
-// one 32-K chunk, four stages in the LDS ring (up to three in flight).
+// one 32-K chunk, four stages in the LDS ring (up to three in flight); the
+// two waves of each SIMD run the ping-pong schedule (one issues a step of
+// MFMAs while the other reads fragments and issues loads).  Measured on the
+// 8B-class prefill: 0.706-0.708 ms against 0.727-0.733 ms for the
+// interleaved schedule of the same tile; a fifth stage, raising the MFMA
+// wave's priority, or issuing the loads before the fragment reads did not
+// help.
 struct WideCfg {
     static constexpr int BM = 256, BN = 256, WGM = 4, WGN = 2, KCS = 1, STAGES = 4;
     static constexpr int GROUP_M = 8;
@@ -50,9 +56,10 @@ hipError_t wide_prepare()
     using C = WideCfg;
     using P = WidePhasedCfg;
     using T = WideTailCfg;
-    hipError_t e = wide_attrs<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_SWIGLU>();
+    hipError_t e =
+        wide_attrs<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_SWIGLU, false, true>();
     if (e == hipSuccess)
-        e = wide_attrs<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_PLAIN>();
+        e = wide_attrs<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI_PLAIN, false, true>();
     if (e == hipSuccess)
         e = wide_attrs<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI_SWIGLU>();
     if (e == hipSuccess)
@@ -71,14 +78,15 @@ static hipError_t launch_wide_epi(const GemmArgs& g, hipStream_t s)
     const int G = full.blocks;
     const int tail = G > WIDE_CUS ? G % WIDE_CUS : 0;
     if (tail == 0 || tail > WIDE_CUS / 2)
-        return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI>(
+        return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI, false, true>(
             g, s, C::GROUP_M, true, &full);
     WideGrid head = full, rest = full;
     head.blocks = G - tail;
     rest.blocks = 4 * tail;
     rest.tail_base = G - tail;
-    hipError_t e = launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI>(
-        g, s, C::GROUP_M, true, &head);
+    hipError_t e =
+        launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI, false, true>(
+            g, s, C::GROUP_M, true, &head);
     if (e == hipSuccess)
         e = launch_wide_cfg<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI>(
             g, s, C::GROUP_M, true, &rest);

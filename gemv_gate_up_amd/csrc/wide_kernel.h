@@ -15,6 +15,10 @@
 //     barrier per stage publishes stage t+1, whose fragments are then read
 //     into registers behind stage t's MFMAs (v_mfma_f32_16x16x32_bf16), so
 //     LDS latency hides behind matrix work;
+//   * or (PP) the ping-pong schedule: the two waves of each SIMD alternate
+//     between a phase of a whole step's MFMAs and a phase of fragment reads
+//     and loads, one barrier per phase, so the matrix unit of every SIMD
+//     always has one wave feeding it;
 //   * pairing block = MFMA N fragment (16 columns): lane l holds gate and up
 //     of the same output element, so the epilogue needs no lane exchange;
 //   * tiles are remapped so each XCD (own L2) works through a compact group
@@ -134,7 +138,7 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 }
 
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED,
-          bool PA, bool PO>
+          bool PA, bool PO, bool PP = false>
 __global__ void __launch_bounds__(WGM * WGN * 64, 1)
 wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, int M,
                  const uint16_t* __restrict__ w, int64_t nkc, int64_t npb,
@@ -148,6 +152,7 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     static_assert(!PHASED || EPI == EPI_SWIGLU, "the phased schedule is for the gate/up pair");
     static_assert(!(PA && KTAIL), "packed activations are zero-padded along K");
     static_assert(!PO || EPI == EPI_SWIGLU, "packed output is the h of the gate/up pair");
+    static_assert(!PP || (!PHASED && NW == 8), "ping-pong: one pass, two groups of four waves");
 
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -325,6 +330,66 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         wait_stage<PPW, STAGES - 2>((int)(rem < STAGES - 2 ? rem : STAGES - 2));
     }
     barrier_lds();
+    f32x4 gs[PHASED ? FM : 1][PHASED ? FN : 1];   // silu(gate) of the phased schedule
+    if constexpr (PP) {
+        // Ping-pong: waves w and w + 4 share a SIMD; group 0 (waves 0-3)
+        // and group 1 (waves 4-7) alternate phases, so on every SIMD one
+        // wave issues a whole step of MFMAs back to back while the other
+        // reads its next step's fragments from LDS and issues its share of
+        // a stage's global -> LDS loads.  Each wave runs mem(0), mem-phase
+        // compute(0), mem(1), compute(1), ...; group 1 starts one phase
+        // later.  A workgroup barrier ends every phase; before the barrier
+        // that precedes a read of stage t by group 0 (the end of an odd
+        // phase), every wave has its own loads of stage t complete, and
+        // every barrier retires the wave's LDS reads, so the slot that a
+        // mem phase reloads (read two phases earlier at the latest) is
+        // free.  One fragment set per wave: a mem phase refills the
+        // registers of the compute phase before it.
+        const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+        AFrags af;
+        BFrags bf;
+        auto mem = [&](int t) {
+            read_a(t, af);
+            const uint8_t* base = stage_ptr(t);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                bf.v[0][fn] = read_b(base, 0, fn);
+            if (t + STAGES - 1 < nsteps)
+                load_stage(t + STAGES - 1);
+        };
+        auto compute = [&]() {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v[0][fm], bf.v[0][fn],
+                                                                          acc[fm][fn], 0, 0, 0);
+        };
+        // stage t + 1 complete in this wave (loads issued up to stage t + STAGES - 1)
+        auto wait_next = [&](int t) {
+            const int ahead = nsteps - 2 - t;
+            wait_stage<PPW, STAGES - 2>(ahead < STAGES - 2 ? ahead : STAGES - 2);
+        };
+        auto phase_end = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            barrier_lds();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        if (grp)
+            phase_end();
+        for (int t = 0; t < nsteps; ++t) {
+            mem(t);
+            if (grp)
+                wait_next(t);
+            phase_end();
+            compute();
+            if (!grp)
+                wait_next(t);
+            phase_end();
+        }
+        if (!grp)
+            phase_end();
+    } else {
     AFrags a0, a1;
     BFrags b;
     read_a(0, a0);
@@ -350,7 +415,6 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     }
     // Phased: the gate tile is finished; keep silu(gate) and run the up pass
     // (its first stages were issued during the gate pass).
-    f32x4 gs[PHASED ? FM : 1][PHASED ? FN : 1];
     if constexpr (PHASED) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -367,6 +431,7 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
             advance(t + 1);
             step(t + 1, a1, a0, b, true);
         }
+    }
     }
 
     // ---- epilogue: lane l holds rows 4*(l/16)+i of column l%16 of each
@@ -463,12 +528,12 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
 // outside any later stream capture when the library's prepare step runs
 // first).
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED,
-          bool PA, bool PO>
+          bool PA, bool PO, bool PP = false>
 static hipError_t wide_attr()
 {
     using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
     static const hipError_t e = hipFuncSetAttribute(
-        (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED, PA, PO>,
+        (const void*)&wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED, PA, PO, PP>,
         hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS_BYTES);
     return e;
 }
@@ -493,18 +558,18 @@ WideGrid wide_full_grid(const GemmArgs& g)
 
 // Host launcher for one instantiation.
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool KTAIL, bool PHASED,
-          bool PA, bool PO>
+          bool PA, bool PO, bool PP = false>
 static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m, bool launch,
                                    const WideGrid* grid)
 {
     using S = WideShape<BM, BN, WGM, WGN, KCS, STAGES, PHASED>;
-    const hipError_t e = wide_attr<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED, PA, PO>();
+    const hipError_t e = wide_attr<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED, PA, PO, PP>();
     if (e != hipSuccess || !launch)
         return e;
     const WideGrid gr = grid ? *grid : wide_full_grid<BM, BN, S::PB_TILE>(g);
     if (gr.blocks <= 0)
         return hipSuccess;
-    wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED, PA, PO>
+    wide_bf16_kernel<BM, BN, WGM, WGN, KCS, STAGES, EPI, KTAIL, PHASED, PA, PO, PP>
         <<<dim3((unsigned)gr.blocks), dim3(S::THREADS), S::LDS_BYTES, s>>>(
             (const uint16_t*)g.a, g.lda, g.geom.K, (int)g.M, (const uint16_t*)g.w, g.geom.nkc,
             g.geom.npb, (uint16_t*)g.out, g.ldo, g.ncols_out, g.out_nkc, gr.tiles_m, gr.tiles_n,
@@ -516,35 +581,38 @@ static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m
 // activations (the latter with a K tail when K is not a whole number of
 // stages), packed or row-major output.  With launch = false it only sets
 // the launch attribute of that instantiation.
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED, bool PO>
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED, bool PO,
+          bool PP = false>
 static hipError_t launch_wide_out(const GemmArgs& g, hipStream_t s, int group_m, bool launch,
                                   const WideGrid* grid)
 {
     if (g.a_packed)
-        return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED, true, PO>(
+        return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED, true, PO, PP>(
             g, s, group_m, launch, grid);
     if (g.geom.K % (KCS * 32) == 0)
-        return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED, false, PO>(
+        return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED, false, PO, PP>(
             g, s, group_m, launch, grid);
-    return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, true, PHASED, false, PO>(
+    return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, true, PHASED, false, PO, PP>(
         g, s, group_m, launch, grid);
 }
 
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED = false>
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED = false,
+          bool PP = false>
 hipError_t launch_wide_cfg(const GemmArgs& g, hipStream_t s, int group_m, bool launch = true,
                            const WideGrid* grid = nullptr)
 {
     if constexpr (EPI == EPI_SWIGLU) {
         if (g.out_nkc > 0)
-            return launch_wide_out<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, true>(
+            return launch_wide_out<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, true, PP>(
                 g, s, group_m, launch, grid);
     }
-    return launch_wide_out<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, false>(g, s, group_m, launch,
-                                                                            grid);
+    return launch_wide_out<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, false, PP>(
+        g, s, group_m, launch, grid);
 }
 
 // Sets the launch attribute of every instantiation of one configuration.
-template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED = false>
+template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED = false,
+          bool PP = false>
 hipError_t wide_attrs()
 {
     GemmArgs g;
@@ -554,7 +622,7 @@ hipError_t wide_attrs()
         g.a_packed = variant % 3 == 2;
         g.geom.K = variant % 3 == 1 ? 1 : 0;   // K tail or not
         g.out_nkc = variant / 3;
-        e = launch_wide_cfg<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED>(g, nullptr, 0, false);
+        e = launch_wide_cfg<BM, BN, WGM, WGN, KCS, STAGES, EPI, PHASED, PP>(g, nullptr, 0, false);
     }
     return e;
 }
