@@ -336,15 +336,16 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         // and group 1 (waves 4-7) alternate phases, so on every SIMD one
         // wave issues a whole step of MFMAs back to back while the other
         // reads its next step's fragments from LDS and issues its share of
-        // a stage's global -> LDS loads.  Each wave runs mem(0), mem-phase
+        // a stage's global -> LDS loads.  Each wave runs mem(0),
         // compute(0), mem(1), compute(1), ...; group 1 starts one phase
         // later.  A workgroup barrier ends every phase; before the barrier
         // that precedes a read of stage t by group 0 (the end of an odd
         // phase), every wave has its own loads of stage t complete, and
         // every barrier retires the wave's LDS reads, so the slot that a
-        // mem phase reloads (read two phases earlier at the latest) is
-        // free.  One fragment set per wave: a mem phase refills the
-        // registers of the compute phase before it.
+        // mem phase reloads (stage t - 1's, last read in the phase before)
+        // is free once the barrier between them has passed.  One fragment
+        // set per wave: a mem phase refills the registers of the compute
+        // phase before it.
         const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
         AFrags af;
         BFrags bf;
@@ -390,48 +391,48 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
         if (!grp)
             phase_end();
     } else {
-    AFrags a0, a1;
-    BFrags b;
-    read_a(0, a0);
-    {
-        const uint8_t* base0 = stage_ptr(0);
+        AFrags a0, a1;
+        BFrags b;
+        read_a(0, a0);
+        {
+            const uint8_t* base0 = stage_ptr(0);
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-            for (int kc = 0; kc < KCS; ++kc)
-                b.v[kc][fn] = read_b(base0, kc, fn);
-    }
-    // Two steps per trip so that both A sets stay in registers.  A pass
-    // always has an even step count (K is padded to two chunks), so there
-    // is no tail: the last refill reads a stale but in-bounds ring slot
-    // whose values are never used.  No LDS read is conditional, so the
-    // compiler's wait counts stay exact, and no peeled copy of the step
-    // raises register pressure past the loop.
-    for (int t = 0; t < kpass; t += 2) {
-        advance(t);
-        step(t, a0, a1, b, true);
-        advance(t + 1);
-        step(t + 1, a1, a0, b, true);
-    }
-    // Phased: the gate tile is finished; keep silu(gate) and run the up pass
-    // (its first stages were issued during the gate pass).
-    if constexpr (PHASED) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    gs[i][j][e] = silu(acc[i][j][e]);
-                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        for (int t = kpass; t < nsteps; t += 2) {
+                for (int kc = 0; kc < KCS; ++kc)
+                    b.v[kc][fn] = read_b(base0, kc, fn);
+        }
+        // Two steps per trip so that both A sets stay in registers.  A pass
+        // always has an even step count (K is padded to two chunks), so there
+        // is no tail: the last refill reads a stale but in-bounds ring slot
+        // whose values are never used.  No LDS read is conditional, so the
+        // compiler's wait counts stay exact, and no peeled copy of the step
+        // raises register pressure past the loop.
+        for (int t = 0; t < kpass; t += 2) {
             advance(t);
             step(t, a0, a1, b, true);
             advance(t + 1);
             step(t + 1, a1, a0, b, true);
         }
-    }
+        // Phased: the gate tile is finished; keep silu(gate) and run the up pass
+        // (its first stages were issued during the gate pass).
+        if constexpr (PHASED) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        gs[i][j][e] = silu(acc[i][j][e]);
+                    acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            for (int t = kpass; t < nsteps; t += 2) {
+                advance(t);
+                step(t, a0, a1, b, true);
+                advance(t + 1);
+                step(t + 1, a1, a0, b, true);
+            }
+        }
     }
 
     // ---- epilogue: lane l holds rows 4*(l/16)+i of column l%16 of each
