@@ -102,7 +102,8 @@ typedef enum swiglu_status {
 typedef enum swiglu_path {
     SWIGLU_PATH_AUTO = 0,      /* dispatcher: few rows -> skinny, many rows -> wide */
     SWIGLU_PATH_SKINNY = 1,    /* split-over-weights kernels (any M, any dtype) */
-    SWIGLU_PATH_WIDE = 2,      /* bf16 MFMA GEMM with LDS double buffering */
+    SWIGLU_PATH_WIDE = 2,      /* bf16 MFMA GEMM over a four-stage LDS ring of operand
+                                  tiles, the two waves of each SIMD in ping-pong */
     /* bf16 MFMA GEMM, two-pass schedule: per output tile a K loop over the
      * gate columns, silu in registers, then a K loop over the up columns
      * (Kernel-1 of "Tile-Level Activation Overlap for Efficient LLM
