@@ -74,6 +74,18 @@ static hipError_t launch_wide_epi(const GemmArgs& g, hipStream_t s)
 {
     using C = WideCfg;
     using T = WideTailCfg;
+    // Up to 128 rows a grid of 256-row tiles leaves most compute units idle
+    // (112 tiles for the 8B-class gate/up product) and the product is bound
+    // by the weight stream: the whole grid runs as 128 x 128 tiles instead
+    // (224 workgroups there).  Measured on that shape: 65 rows 85.6 -> 57.3
+    // us, 96 rows 87.9 -> 59.5 us, 128 rows 89.9 -> 63.4 us; the 72B-class
+    // product at 128 rows 228.5 -> 219.2 us; from 192 rows on the 256-row
+    // tiles are faster.  Same MFMAs in the same K order: same results.
+    if (g.M <= WideTailCfg::BM) {
+        WideGrid q = wide_full_grid<T::BM, T::BN, T::BN / 32>(g);
+        return launch_wide_cfg<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI>(
+            g, s, C::GROUP_M, true, &q);
+    }
     WideGrid full = wide_full_grid<C::BM, C::BN, C::BN / 32>(g);
     const int G = full.blocks;
     const int tail = G > WIDE_CUS ? G % WIDE_CUS : 0;
