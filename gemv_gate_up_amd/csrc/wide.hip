@@ -41,6 +41,12 @@ struct WideTailCfg {
 };
 static_assert(2 * WideTailCfg::BM == WideCfg::BM && 2 * WideTailCfg::BN == WideCfg::BN,
               "quarter tiles");
+// For batches whose 256 x 256 grid would fill at most half the compute
+// units: 256 rows by 4 pair blocks (8 waves of 64 x 64, ping-pong), six
+// stages of 24 KB.
+struct WideHalfCfg {
+    static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 2, KCS = 1, STAGES = 6;
+};
 constexpr int WIDE_CUS = 256;   // MI355X compute units: one 256 x 256 tile each per round
 
 int wide_supported(const GemmArgs& g)
@@ -66,6 +72,11 @@ hipError_t wide_prepare()
         e = wide_attrs<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI_PLAIN>();
     if (e == hipSuccess)
         e = wide_attrs<P::BM, P::BN, P::WGM, P::WGN, P::KCS, P::STAGES, EPI_SWIGLU, true>();
+    using H = WideHalfCfg;
+    if (e == hipSuccess)
+        e = wide_attrs<H::BM, H::BN, H::WGM, H::WGN, H::KCS, H::STAGES, EPI_SWIGLU, false, true>();
+    if (e == hipSuccess)
+        e = wide_attrs<H::BM, H::BN, H::WGM, H::WGN, H::KCS, H::STAGES, EPI_PLAIN, false, true>();
     return e;
 }
 
@@ -74,20 +85,27 @@ static hipError_t launch_wide_epi(const GemmArgs& g, hipStream_t s)
 {
     using C = WideCfg;
     using T = WideTailCfg;
-    // Up to 128 rows a grid of 256-row tiles leaves most compute units idle
-    // (112 tiles for the 8B-class gate/up product) and the product is bound
-    // by the weight stream: the whole grid runs as 128 x 128 tiles instead
-    // (224 workgroups there).  Measured on that shape: 65 rows 85.6 -> 57.3
-    // us, 96 rows 87.9 -> 59.5 us, 128 rows 89.9 -> 63.4 us; the 72B-class
-    // product at 128 rows 228.5 -> 219.2 us; from 192 rows on the 256-row
-    // tiles are faster.  Same MFMAs in the same K order: same results.
-    if (g.M <= WideTailCfg::BM) {
-        WideGrid q = wide_full_grid<T::BM, T::BN, T::BN / 32>(g);
-        return launch_wide_cfg<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI>(
-            g, s, C::GROUP_M, true, &q);
-    }
     WideGrid full = wide_full_grid<C::BM, C::BN, C::BN / 32>(g);
     const int G = full.blocks;
+    // A grid of 256 x 256 tiles that fills at most half the compute units
+    // (a batch of a few hundred rows: 112 tiles for the 8B-class gate/up
+    // product up to 256 rows) leaves most of them idle while the product is
+    // bound by the weight stream; the whole grid then runs as twice as many
+    // narrower tiles: 128 x 128 up to 128 rows, 256 x 128 above.  Measured
+    // on that shape: 65, 96, 128 rows 85.6, 87.9, 89.9 -> 57-61, 60-67,
+    // 63-69 us; 192, 256 rows 95.7, 100.8 -> 88.4, 92.6 us.  Every output
+    // sums the same MFMAs in the same K order, so the results are the same.
+    if (G <= WIDE_CUS / 2) {
+        if (g.M <= T::BM) {
+            WideGrid q = wide_full_grid<T::BM, T::BN, T::BN / 32>(g);
+            return launch_wide_cfg<T::BM, T::BN, T::WGM, T::WGN, T::KCS, T::STAGES, EPI>(
+                g, s, C::GROUP_M, true, &q);
+        }
+        using H = WideHalfCfg;
+        WideGrid q = wide_full_grid<H::BM, H::BN, H::BN / 32>(g);
+        return launch_wide_cfg<H::BM, H::BN, H::WGM, H::WGN, H::KCS, H::STAGES, EPI, false, true>(
+            g, s, C::GROUP_M, true, &q);
+    }
     const int tail = G > WIDE_CUS ? G % WIDE_CUS : 0;
     if (tail == 0 || tail > WIDE_CUS / 2)
         return launch_wide_cfg<C::BM, C::BN, C::WGM, C::WGN, C::KCS, C::STAGES, EPI, false, true>(
