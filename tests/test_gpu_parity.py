@@ -242,8 +242,15 @@ def test_paths_agree_where_both_apply():
     assert np.all(np.abs(a - b) <= 2 * 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-3)
 
 
+# The one-pass schedule picks its tile from the grid: 128 x 128 up to 128 rows
+# and 256 x 128 above while a grid of 256 x 256 tiles would have at most 128
+# of them, 256 x 256 otherwise.  (128, 256, 1024) and (129, 256, 1024) sit on
+# either side of the row boundary, (256, 64, 16384) and (256, 64, 16512) on
+# either side of the tile-count boundary (128 and 129 tiles), (1024, 256,
+# 4224) has 132 tiles of 256 x 256.
 @pytest.mark.parametrize("shape", [(96, 768, 1024), (300, 1000, 1400), (257, 520, 2056),
-                                   (1024, 4096, 1536)])
+                                   (1024, 4096, 1536), (128, 256, 1024), (129, 256, 1024),
+                                   (256, 64, 16384), (256, 64, 16512), (1024, 256, 4224)])
 def test_two_pass_schedule_is_bitwise_the_one_pass_result(shape):
     # Both schedules sum every accumulator over the same MFMAs in the same
     # K order and apply silu(gate) * up in fp32, so they agree bit for bit.
