@@ -514,10 +514,14 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // its few 32-column blocks are better spread over more workgroups; with
     // bf16 weights eight waves share each workgroup's K range, halving the
     // serial load-to-MFMA trips per wave (the 0.5B-class MLP at 64 rows:
-    // gate/up 11.0 -> 10.2 us, down 11.8 -> 11.2 us)
-    case 2: pick_split_bf16<2, Q ? 2 : 4, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
-    case 3: pick_split_bf16<3, WF == WF_MXFP4 ? 1 : 2, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
-    default: pick_split_bf16<4, WF == WF_MXFP4 ? 1 : 2, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
+    // gate/up 11.0 -> 10.2 us, down 11.8 -> 11.2 us), each with one piece
+    // per half in flight: fewer registers (120 instead of 155 at 64 rows)
+    // outweigh the extra trip (8B-class gate/up at 32, 48 and 64 rows 52.4,
+    // 56.4, 64.4 -> 46.5, 52.5, 60.8 us; 0.5B-class MLP at 64 rows 22.2 ->
+    // 21.4 us)
+    case 2: pick_split_bf16<2, Q ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
+    case 3: pick_split_bf16<3, WF == WF_FP8 ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
+    default: pick_split_bf16<4, WF == WF_FP8 ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
     }
 }
 
