@@ -35,12 +35,14 @@ static_assert(WideCfg::BN / 32 == WidePhasedCfg::BN / 16, "both schedules tile 8
 // but the same load latency to hide, hence its deeper ring (8 stages of
 // 16 KB).  Measured on the 72B-class gate/up product: the tail round
 // 213 -> about 95 us.  Every output sums the same MFMAs in the same K
-// order, so the results are the same bit for bit.
+// order, so the results are the same bit for bit.  The same instantiation
+// runs whole grids of up to 128 rows (launch_wide_epi).
 struct WideTailCfg {
     static constexpr int BM = 128, BN = 128, WGM = 4, WGN = 2, KCS = 1, STAGES = 8;
 };
 static_assert(2 * WideTailCfg::BM == WideCfg::BM && 2 * WideTailCfg::BN == WideCfg::BN,
               "quarter tiles");
+
 // For batches whose 256 x 256 grid would fill at most half the compute
 // units: 256 rows by 4 pair blocks (8 waves of 64 x 64, ping-pong), six
 // stages of 24 KB.
