@@ -486,10 +486,13 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // per wave when that still leaves a workgroup per CU (measured
             // at 1, 8 and 16 rows on the 8B and 72B shapes); up to 4 rows,
             // eight waves per workgroup (8B decode at one row 14.1 -> 13.3
-            // us, 72B 45.0 -> 44.0 us; slower at 8 rows on the 8B shape)
+            // us, 72B 45.0 -> 44.0 us; slower at 8 rows on the 8B shape),
+            // and so does a down product above 8 rows (the 72B-class MLP at
+            // 16 rows 91.5 -> 84.2 us; an 8B-class gate/up product at 16
+            // rows is slower with eight: 15.7 -> 16.9 us)
             if (g.M > 8 && p.grid_pb >= 4 * MXFP4_WIDE_PB_CUS)
                 pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
-            else if (g.M <= 4)
+            else if (g.M <= 4 || (EPI == EPI_PLAIN && g.M > 8))
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else
                 pick_split_bf16<1, 1, 2, EPI, WF>(g, p, partial, s);
