@@ -499,9 +499,13 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
         } else if constexpr (Q) {
             // FP8: up to 2 rows, eight waves per workgroup (8B decode at one
             // row 21.4 -> 21.0 us, two rows 21.1 -> 20.9 us; at four rows
-            // 21.0 -> 21.4 us)
+            // 21.0 -> 21.4 us); a down product above 8 rows also on eight
+            // waves, one piece per half in flight (72B-class MLP at 16 rows
+            // 130.4 -> 127.4 us)
             if (g.M <= 2)
                 pick_split_bf16<1, 2, 2, EPI, WF, 8>(g, p, partial, s);
+            else if (EPI == EPI_PLAIN && g.M > 8)
+                pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else
                 pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
         } else {
