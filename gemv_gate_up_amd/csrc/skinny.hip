@@ -359,6 +359,11 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
 
 // ---------------------------------------------------------------- second pass
 // Adds the K slices in ascending slice order, then applies the epilogue.
+// The slices are loaded eight at a time before they are added, so a thread
+// waits for one memory round trip per eight slices rather than per slice;
+// the additions keep their order (a slice past S adds nothing, not +0).
+constexpr int RED_BATCH = 8;
+
 template <int EPI, typename OutT>
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(const float* __restrict__ partial, int S, int M, int64_t npc,
@@ -369,19 +374,39 @@ splitk_reduce_kernel(const float* __restrict__ partial, int S, int M, int64_t np
     const int64_t col = (int64_t)(blockIdx.x % col_blocks) * 256 + threadIdx.x;
     if (col >= ncols_out)
         return;
+    const int64_t slice = (int64_t)M * npc;   // floats per slice
     if (EPI == EPI_SWIGLU) {
-        const int64_t pc = (col / 16) * 32 + (col % 16);
+        const float* pr = partial + (int64_t)row * npc + (col / 16) * 32 + (col % 16);
         float g = 0.f, u = 0.f;
-        for (int s = 0; s < S; ++s) {
-            const float* pr = partial + ((int64_t)s * M + row) * npc + pc;
-            g += pr[0];
-            u += pr[16];
+        for (int s0 = 0; s0 < S; s0 += RED_BATCH) {
+            float tg[RED_BATCH], tu[RED_BATCH];
+#pragma unroll
+            for (int j = 0; j < RED_BATCH; ++j) {
+                tg[j] = s0 + j < S ? pr[(s0 + j) * slice] : 0.f;
+                tu[j] = s0 + j < S ? pr[(s0 + j) * slice + 16] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < RED_BATCH; ++j) {
+                if (s0 + j < S) {
+                    g += tg[j];
+                    u += tu[j];
+                }
+            }
         }
         store_out(out + (int64_t)row * ldo + col, silu(g) * u);
     } else {
+        const float* pr = partial + (int64_t)row * npc + col;
         float v = 0.f;
-        for (int s = 0; s < S; ++s)
-            v += partial[((int64_t)s * M + row) * npc + col];
+        for (int s0 = 0; s0 < S; s0 += RED_BATCH) {
+            float t[RED_BATCH];
+#pragma unroll
+            for (int j = 0; j < RED_BATCH; ++j)
+                t[j] = s0 + j < S ? pr[(s0 + j) * slice] : 0.f;
+#pragma unroll
+            for (int j = 0; j < RED_BATCH; ++j)
+                if (s0 + j < S)
+                    v += t[j];
+        }
         store_out(out + (int64_t)row * ldo + col, plain_tail(v, resid, ldr, bias, row, col));
     }
 }
