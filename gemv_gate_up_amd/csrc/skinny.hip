@@ -289,21 +289,38 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
                 wu[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
+        // The activation vectors are loaded before any of them is used:
+        // every piece's at once when they fit in a few registers (the
+        // one-row decode: 8 loads in flight instead of 8 round trips one
+        // after another), else a piece's rows at once.  The FMAs keep their
+        // order.
+        constexpr int XB = U * RT <= 16 ? U : 1;   // pieces whose vectors are loaded together
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t kc = kb + SK_WAVES * u;
-            const int64_t k = kc * 16 + koff;
+        for (int u0 = 0; u0 < U; u0 += XB) {
+            f32x4 xv[XB][RT];
 #pragma unroll
-            for (int r = 0; r < RT; ++r) {
-                const int row = rbase + r;
-                if (row < M) {   // uniform across the wave
-                    f32x4 xv = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if (kc < kend && k < kvalid)
-                        xv = *(const f32x4*)(a + (int64_t)row * lda + k);
+            for (int i = 0; i < XB; ++i) {
+                const int64_t kc = kb + SK_WAVES * (u0 + i);
+                const int64_t k = kc * 16 + koff;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        accg[r] = __builtin_fmaf(xv[e], wg[u][e], accg[r]);
-                        accu[r] = __builtin_fmaf(xv[e], wu[u][e], accu[r]);
+                for (int r = 0; r < RT; ++r) {
+                    const int row = rbase + r;
+                    xv[i][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (row < M && kc < kend && k < kvalid)
+                        xv[i][r] = *(const f32x4*)(a + (int64_t)row * lda + k);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < XB; ++i) {
+                const int u = u0 + i;
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    if (rbase + r < M) {   // uniform across the wave
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            accg[r] = __builtin_fmaf(xv[i][r][e], wg[u][e], accg[r]);
+                            accu[r] = __builtin_fmaf(xv[i][r][e], wu[u][e], accu[r]);
+                        }
                     }
                 }
             }
