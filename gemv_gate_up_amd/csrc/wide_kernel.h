@@ -457,6 +457,100 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
     (void)gs;
     const int c = lane & 15;
     // fragment j of the wave holds output column wn * WOW + 16 * j + c
+    // Plain products: the lane's bias values are loaded once, before any
+    // is added.  Inside the output the arithmetic is the plain tail's
+    // (bias, then residual, in fp32, one rounding); values outside it are
+    // never stored.
+    float bv[EPI == EPI_PLAIN ? FO : 1];
+    if constexpr (EPI == EPI_PLAIN) {
+#pragma unroll
+        for (int j = 0; j < FO; ++j) {
+            const int64_t gcol = col0 + wn * WOW + 16 * j + c;
+            bv[j] = bias && gcol < ncols_out ? bf16_to_f32(bias[gcol]) : 0.f;
+        }
+    }
+    (void)bv;
+    if constexpr (EPI == EPI_PLAIN) {
+        if (resid) {
+            // With a residual (the MLP block's down product) the products
+            // are staged in LDS as fp32, and the bias and the residual are
+            // read like the output: whole 16-byte vectors, all of a thread's
+            // vectors of a pass issued before the first is used.
+            constexpr int LROWF = OW + 4;   // padded LDS row, floats
+            constexpr int WRF_FIT = S::LDS_BYTES / (S::WTM * LROWF * 4);
+            constexpr int WRPF = WRF_FIT >= WGM ? WGM : (WRF_FIT >= WGM / 2 ? WGM / 2 : 1);
+            constexpr int PROWSF = WRPF * S::WTM;
+            constexpr int ITER = PROWSF * VPR / S::THREADS;   // vectors per thread and pass
+            static_assert(WRPF >= 1 && WGM % WRPF == 0 && PROWSF * LROWF * 4 <= S::LDS_BYTES,
+                          "fp32 staging fits the ring");
+            static_assert(ITER >= 1 && ITER * S::THREADS == PROWSF * VPR, "whole vectors per thread");
+            float* epf = (float*)smem;
+            // the tile's residual rows; a row past the output reads zeros
+            const uint32_t rbytes = (uint32_t)((int64_t)rows_here * ldr * 2);
+            const __amdgpu_buffer_rsrc_t rres = make_rsrc(resid + (int64_t)m0 * ldr, rbytes);
+            // a thread's columns are the same in every pass and vector
+            static_assert(S::THREADS % VPR == 0, "fixed columns per thread");
+            float bcol[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t col = col0 + (threadIdx.x % VPR) * 8 + e;
+                bcol[e] = bias && col < ncols_out ? bf16_to_f32(bias[col]) : 0.f;
+            }
+#pragma unroll 1
+            for (int pass = 0; pass < WGM / WRPF; ++pass) {
+                i32x4 rr[ITER];
+#pragma unroll
+                for (int it = 0; it < ITER; ++it) {
+                    const int v = threadIdx.x + it * S::THREADS;
+                    const int r = pass * PROWSF + v / VPR;
+                    const uint32_t off =
+                        r < rows_here ? (uint32_t)(((int64_t)r * ldr + col0 + (v % VPR) * 8) * 2)
+                                      : rbytes;
+                    rr[it] = __builtin_amdgcn_raw_buffer_load_b128(rres, off, 0, 0);
+                }
+                __syncthreads();   // ring reads (first pass) or previous reads (later) are done
+                if (wm / WRPF == pass) {
+                    const int rbase = (wm % WRPF) * S::WTM;
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                        for (int j = 0; j < FO; ++j)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int r = rbase + fm * 16 + (lane >> 4) * 4 + i;
+                                epf[r * LROWF + wn * WOW + 16 * j + c] = acc[fm][j][i];
+                            }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int it = 0; it < ITER; ++it) {
+                    const int v = threadIdx.x + it * S::THREADS;
+                    const int r = v / VPR, cv = v % VPR;
+                    const int row = m0 + pass * PROWSF + r;
+                    const int64_t col = col0 + cv * 8;
+                    if (row < M && col < ncols_out) {
+                        const float* src = epf + r * LROWF + cv * 8;
+                        const i32x4 rv = rr[it];
+                        i32x4 o;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t w = (uint32_t)rv[q];
+                            float lo = src[2 * q], hi = src[2 * q + 1];
+                            if (bias) {
+                                lo += bcol[2 * q];
+                                hi += bcol[2 * q + 1];
+                            }
+                            lo += bf16_to_f32((uint16_t)w);
+                            hi += bf16_to_f32((uint16_t)(w >> 16));
+                            o[q] = (int)((uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16));
+                        }
+                        *(i32x4*)(out + (int64_t)row * ldo + col) = o;
+                    }
+                }
+            }
+            return;
+        }
+    }
     uint16_t res[FM][FO][4];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -471,11 +565,8 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
                     v = silu(acc[fm][2 * j][i]) * acc[fm][2 * j + 1][i];
                 } else {
                     v = acc[fm][j][i];
-                    // bias and residual only inside the output
-                    const int64_t grow = m0 + wm * S::WTM + fm * 16 + (lane >> 4) * 4 + i;
-                    const int64_t gcol = col0 + wn * WOW + 16 * j + c;
-                    if ((resid || bias) && grow < M && gcol < ncols_out)
-                        v = plain_tail(v, resid, ldr, bias, grow, gcol);
+                    if (bias)
+                        v += bv[j];
                 }
                 res[fm][j][i] = f32_to_bf16(v);
             }

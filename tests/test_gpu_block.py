@@ -81,16 +81,32 @@ def test_block_in_place_equals_out_of_place(case):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("path", [sw.SWIGLU_PATH_SKINNY, sw.SWIGLU_PATH_WIDE])
-def test_zero_down_weight_gives_rounded_residual_plus_bias(path):
-    # h . 0 = 0 exactly, so out = round(r + bias); with bf16 r and bias the
-    # fp32 sum is exact here, so the result is the nearest bf16 of it
-    M, d, dff = 80, 256, 384
+# (M, d, dff, path): besides the small case, two wide-path down products
+# whose residual epilogue runs in 256 x 256 tiles with ragged rows and
+# columns (9 x 17 tiles), and in 7 rounds of them plus quarter tiles for the
+# last (9 x 30 tiles)
+ZERO_DOWN = [(80, 256, 384, sw.SWIGLU_PATH_SKINNY), (80, 256, 384, sw.SWIGLU_PATH_WIDE),
+             (2100, 4104, 256, sw.SWIGLU_PATH_WIDE), (2100, 7560, 256, sw.SWIGLU_PATH_WIDE)]
+
+
+@pytest.mark.parametrize("case", ZERO_DOWN)
+@pytest.mark.parametrize("bias", [True, False])
+def test_zero_down_weight_gives_rounded_residual_plus_bias(case, bias):
+    # h . 0 = 0 exactly, so out = round(0 + r + bias); with bf16 r and bias
+    # the fp32 sum is exact here, so the result is the nearest bf16 of it.
+    # The products' sum starts from +0, so a residual of -0 (a bf16 draw
+    # that rounds to it) gives +0 without a bias (IEEE: +0 + -0 = +0).
+    M, d, dff, path = case
+    say("zero down", case, "bias", bias)
     inp = _block_inputs(11, M, d, dff, BF16)
     inp["wd"] = np.zeros_like(inp["wd"])
     wp, wdp = pack(inp, d, dff, BF16)
-    out = _run(inp, wp, wdp, M, d, dff, BF16, path=path).cpu().numpy().view(np.uint16)
-    want = wl.f32_to_bf16_bits((wl.bf16_bits_to_f32(inp["r"]).astype(np.float64)
-                                + wl.bf16_bits_to_f32(inp["bias"]).astype(np.float64)
-                                ).astype(np.float32))
-    assert np.array_equal(out, want)
+    out = _run(inp, wp, wdp, M, d, dff, BF16, bias, path).cpu().numpy().view(np.uint16)
+    want = 0.0 + wl.bf16_bits_to_f32(inp["r"]).astype(np.float64)
+    if bias:
+        want = want + wl.bf16_bits_to_f32(inp["bias"]).astype(np.float64)
+    want = wl.f32_to_bf16_bits(want.astype(np.float32))
+    bad = np.argwhere(out != want)
+    assert bad.size == 0, "%d mismatches, rows %s, columns %s, first %s: %s != %s" % (
+        len(bad), np.unique(bad[:, 0])[:12], np.unique(bad[:, 1])[:12], bad[:4].tolist(),
+        wl.bf16_bits_to_f32(out[tuple(bad[:4].T)]), wl.bf16_bits_to_f32(want[tuple(bad[:4].T)]))
