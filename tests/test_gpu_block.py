@@ -110,3 +110,22 @@ def test_zero_down_weight_gives_rounded_residual_plus_bias(case, bias):
     assert bad.size == 0, "%d mismatches, rows %s, columns %s, first %s: %s != %s" % (
         len(bad), np.unique(bad[:, 0])[:12], np.unique(bad[:, 1])[:12], bad[:4].tolist(),
         wl.bf16_bits_to_f32(out[tuple(bad[:4].T)]), wl.bf16_bits_to_f32(want[tuple(bad[:4].T)]))
+
+
+# The down product on 256 x 256 tiles (9 x 17 of them, ragged rows and
+# columns), and on 7 rounds of them plus quarter tiles for the last (9 x 30):
+# the tile's products are staged in LDS a quarter at a time and the bias and
+# residual added as the rows are written; sampled rows cover every quarter.
+@pytest.mark.parametrize("shape", [(2100, 4104, 1024), (2100, 7560, 512)])
+@pytest.mark.parametrize("bias", [True, False])
+def test_block_on_full_tiles_against_the_oracle(shape, bias):
+    M, d, dff = shape
+    say("block full tiles", shape, "bias", bias)
+    inp = _block_inputs(5 + M + d, M, d, dff, BF16)
+    wp, wdp = pack(inp, d, dff, BF16)
+    out = host(_run(inp, wp, wdp, M, d, dff, BF16, bias, sw.SWIGLU_PATH_WIDE), BF16)
+    rows = sorted({0, 63, 64, 127, 128, 191, 192, 255, 256, 1791, 1792, 2047, 2048, M - 1}
+                  | set(range(5, M, 89)))
+    ref = oracle.mlp_block(inp["r"], inp["gamma"], EPS, inp["wg"], inp["wu"], inp["wd"],
+                           bias=inp["bias"] if bias else None, rows=rows)
+    say(assert_close(out[rows], ref, BF16, "block full tiles %s" % (shape,)))
