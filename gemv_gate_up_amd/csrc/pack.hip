@@ -207,26 +207,40 @@ pack_mxfp4_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict_
     dst[v] = i32x4{(int)word[0], (int)word[1], (int)word[2], (int)word[3]};
 }
 
-// Activations into the packed layout of geometry.h, one thread per 16-byte
-// vector of the output: the 64 threads of a piece read 16 rows x 64
-// contiguous bytes and write the piece as one 1 KB run.  Vectors of padded
-// rows or K are zero.  K is a multiple of 8, so a vector is all valid or all
-// padding.
+// Activations into the packed layout of geometry.h, four 16-byte vectors of
+// the output per thread (a workgroup covers 1,024 consecutive vectors, the
+// thread's four 256 apart, all four loads issued before the first store): the
+// 64 threads of a piece read 16 rows x 64 contiguous bytes and write the
+// piece as one 1 KB run.  Vectors of padded rows or K are zero.  K is a
+// multiple of 8, so a vector is all valid or all padding.
+constexpr int PACK_ACT_VPT = 4;
+
 __global__ void __launch_bounds__(256)
 pack_act_kernel(const uint16_t* __restrict__ x, int64_t lda, int64_t M, int64_t K, int64_t nkc,
                 uint16_t* __restrict__ dst, int64_t total_vecs)
 {
-    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (v >= total_vecs)
-        return;
-    const int lane = (int)(v % PIECE_VECS);
-    const int64_t piece = v / PIECE_VECS;
-    const int64_t row = (piece / nkc) * 16 + lane % 16;
-    const int64_t k = (piece % nkc) * 32 + (lane / 16) * 8;
-    i32x4 val = {0, 0, 0, 0};
-    if (row < M && k < K)
-        val = *(const i32x4*)(x + row * lda + k);
-    *(i32x4*)(dst + v * 8) = val;
+    const int64_t v0 = (int64_t)blockIdx.x * (256 * PACK_ACT_VPT) + threadIdx.x;
+    i32x4 val[PACK_ACT_VPT];
+    bool ok[PACK_ACT_VPT];
+#pragma unroll
+    for (int j = 0; j < PACK_ACT_VPT; ++j) {
+        const int64_t v = v0 + j * 256;
+        const int lane = (int)(v % PIECE_VECS);
+        // pieces number at most 2^14 row blocks x 2^15 chunks: 32-bit
+        const uint32_t piece = (uint32_t)(v / PIECE_VECS), kcs = (uint32_t)nkc;
+        const int64_t row = (int64_t)(piece / kcs) * 16 + lane % 16;
+        const int64_t k = (int64_t)(piece % kcs) * 32 + (lane / 16) * 8;
+        // every lane loads (padding lanes the first vector of x, then
+        // discarded), so the four loads issue back to back without branches
+        ok[j] = v < total_vecs && row < M && k < K;
+        val[j] = *(const i32x4*)(x + (ok[j] ? row * lda + k : 0));
+    }
+#pragma unroll
+    for (int j = 0; j < PACK_ACT_VPT; ++j) {
+        const int64_t v = v0 + j * 256;
+        if (v < total_vecs)
+            *(i32x4*)(dst + v * 8) = ok[j] ? val[j] : i32x4{0, 0, 0, 0};
+    }
 }
 
 hipError_t launch_pack_act(const void* x, int64_t lda, int64_t M, int64_t K, int64_t nkc, void* dst,
@@ -235,7 +249,7 @@ hipError_t launch_pack_act(const void* x, int64_t lda, int64_t M, int64_t K, int
     const int64_t total = act_packed_bytes(M, nkc) / 16;
     if (total == 0)
         return hipSuccess;
-    pack_act_kernel<<<dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s>>>(
+    pack_act_kernel<<<dim3((unsigned)ceil_div(total, 256 * PACK_ACT_VPT)), dim3(256), 0, s>>>(
         (const uint16_t*)x, lda, M, K, nkc, (uint16_t*)dst, total);
     return hipGetLastError();
 }

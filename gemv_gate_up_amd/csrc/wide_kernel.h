@@ -28,7 +28,9 @@
 //     16-byte vectors;
 //   * a launch may cover only part of the tile grid: the full rounds, or
 //     (tail_base >= 0) the last partial round as quarter tiles.
-// The down projection runs through the same kernel with a plain epilogue.
+// The down projection runs through the same kernel with a plain epilogue;
+// with a residual (the MLP block) that epilogue stages fp32 products and adds
+// the bias and the residual as the rows are written.
 //
 // PA: the left operand is in the packed activation layout of geometry.h, so
 // that each of its loads is one contiguous 1 KB piece (a row-major tile
@@ -437,11 +439,12 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
 
     // ---- epilogue: lane l holds rows 4*(l/16)+i of column l%16 of each
     // fragment.  Every wave first turns its accumulators into the finished
-    // bf16 values in registers (silu(gate) * up, or the plain product with
-    // bias and residual), all waves at once; the values are then staged in
-    // LDS (the ring is free by now) as many wave-rows at a time as fit (the
-    // whole tile for the gate/up product) and written to memory as whole
-    // rows of 16-byte vectors, so every global write covers full lines.
+    // bf16 values in registers (silu(gate) * up, or the plain product plus
+    // bias), all waves at once; the values are then staged in LDS (the ring
+    // is free by now) as many wave-rows at a time as fit (the whole tile for
+    // the gate/up product) and written to memory as whole rows of 16-byte
+    // vectors, so every global write covers full lines.  A plain product
+    // with a residual stages fp32 values instead (below).
     constexpr int OW = EPI == EPI_SWIGLU && !PHASED ? BN / 2 : BN;   // output columns of the tile
     constexpr int WOW = OW / WGN;                          // of one wave
     constexpr int FO = WOW / 16;                           // output fragments across a wave
@@ -486,6 +489,7 @@ wide_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid, in
             static_assert(ITER >= 1 && ITER * S::THREADS == PROWSF * VPR, "whole vectors per thread");
             float* epf = (float*)smem;
             // the tile's residual rows; a row past the output reads zeros
+            // (at most 256 rows of 2^20 columns: well inside 32-bit offsets)
             const uint32_t rbytes = (uint32_t)((int64_t)rows_here * ldr * 2);
             const __amdgpu_buffer_rsrc_t rres = make_rsrc(resid + (int64_t)m0 * ldr, rbytes);
             // a thread's columns are the same in every pass and vector
