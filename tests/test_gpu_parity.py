@@ -10,8 +10,8 @@ import pytest
 import gemv_gate_up_amd as sw
 import oracle
 import workloads as wl
-from swiglu_testlib import (TOL, assert_close, compare, dev, host, pack, run_mlp, run_up, say,
-                            torch_mod)
+from swiglu_testlib import (TOL, assert_close, bytes_buf, compare, dev, host, pack, run_mlp,
+                            run_up, say, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,11 +111,19 @@ MLP_SHAPES = [(1, 256, 512, BF16), (7, 136, 392, BF16), (64, 896, 4864, BF16),
 @pytest.mark.parametrize("path", [AUTO, SKINNY, WIDE, PHASED])
 def test_mlp_random(shape, path):
     M, d, dff, dtype = shape
-    if path in (WIDE, PHASED) and dtype == F32:
-        pytest.skip("the wide path is bf16 only")
     say("mlp", shape, "path", path)
     inp = wl.random_inputs(M + 3 * d, M, d, dff, dtype, with_down=True)
     wp, wdp = pack(inp, d, dff, dtype)
+    if path in (WIDE, PHASED) and dtype == F32:
+        # the wide path is bf16 only: the forced call is rejected before any
+        # launch and leaves the output as it was
+        y = dev(np.full((M, d), 7.0, np.float32))
+        ws = bytes_buf(1 << 20)
+        rc = sw.mlp_forward_ex(dev(inp["x"]), wp, wdp, y, M, d, dff, dtype, ws, 1 << 20, None, path)
+        torch_mod().cuda.synchronize()
+        assert rc == sw.SWIGLU_ERR_UNSUPPORTED
+        assert np.all(y.cpu().numpy() == 7.0)
+        return
     y = host(run_mlp(dev(inp["x"]), wp, wdp, M, d, dff, dtype, path), dtype)
     ref = oracle.mlp(inp["x"], inp["wg"], inp["wu"], inp["wd"])
     assert_close(y, ref, dtype, "mlp %s path %d" % (shape, path))
