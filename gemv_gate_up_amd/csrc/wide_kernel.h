@@ -674,9 +674,14 @@ static hipError_t launch_wide_inst(const GemmArgs& g, hipStream_t s, int group_m
 }
 
 // Picks the instantiation for the operand layouts of g: packed or row-major
-// activations (the latter with a K tail when K is not a whole number of
-// stages), packed or row-major output.  With launch = false it only sets
-// the launch attribute of that instantiation.
+// activations, packed or row-major output.  Row-major activations take the
+// K-tail variant whenever the weight's chunks reach past K (K not a whole
+// number of stages, or K padded by a chunk to the weight's even chunk
+// count): the lanes of those chunks would otherwise read the next row's
+// first values, or past the end of the last row, and multiply them by the
+// zero padding of the weights, where an Inf or NaN would still poison the
+// sum.  With launch = false it only sets the launch attribute of that
+// instantiation.
 template <int BM, int BN, int WGM, int WGN, int KCS, int STAGES, int EPI, bool PHASED, bool PO,
           bool PP = false>
 static hipError_t launch_wide_out(const GemmArgs& g, hipStream_t s, int group_m, bool launch,
@@ -685,7 +690,7 @@ static hipError_t launch_wide_out(const GemmArgs& g, hipStream_t s, int group_m,
     if (g.a_packed)
         return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED, true, PO, PP>(
             g, s, group_m, launch, grid);
-    if (g.geom.K % (KCS * 32) == 0)
+    if (g.geom.K == g.geom.nkc * 32)
         return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, false, PHASED, false, PO, PP>(
             g, s, group_m, launch, grid);
     return launch_wide_inst<BM, BN, WGM, WGN, KCS, STAGES, EPI, true, PHASED, false, PO, PP>(

@@ -12,6 +12,20 @@ BF16, F32 = sw.SWIGLU_BF16, sw.SWIGLU_F32
 FAKE = 0x10000000    # 16-byte aligned address that is never dereferenced here
 
 
+def rejected_before_launch(create, direct, expected):
+    """Checks a fake-pointer call whose rejection depends on the planner
+    (the workspace it needs).  The graph-creation variant with the same
+    arguments runs the same validation first, without any HIP call, and a
+    recording never executes a kernel; only when it returns the expected
+    status is the direct call made, so a planner change that made the call
+    valid fails here instead of launching a kernel on a fake address."""
+    rc, h = create()
+    if h:
+        sw.swiglu_graph_destroy(h)
+    assert rc == expected, sw.swiglu_status_string(rc)
+    assert direct() == expected
+
+
 def test_header_symbols_are_exported():
     names = sw.header_functions()
     assert {"swiglu_pack_weights", "swiglu_up", "mlp_forward", "swiglu_pack_down"} <= set(names)
@@ -93,11 +107,18 @@ def test_argument_errors_return_before_any_launch(dtype):
 
 def test_workspace_too_small_is_rejected():
     # a split-K decode needs partials; none are given
-    rc = sw.swiglu_up(FAKE, FAKE, FAKE, 1, 4096, 512, F32, None, 0, stream=0)
-    assert rc == sw.SWIGLU_ERR_WORKSPACE
+    assert sw.swiglu_workspace_bytes(1, 4096, 512, F32, 0) > 0
+    rejected_before_launch(
+        lambda: sw.swiglu_up_graph_create(FAKE, FAKE, FAKE, 1, 4096, 512, F32, None, 0),
+        lambda: sw.swiglu_up(FAKE, FAKE, FAKE, 1, 4096, 512, F32, None, 0, stream=0),
+        sw.SWIGLU_ERR_WORKSPACE)
     need = sw.swiglu_workspace_bytes(64, 896, 4864, BF16, 1)
-    rc = sw.mlp_forward(FAKE, FAKE, FAKE, FAKE, 64, 896, 4864, BF16, FAKE, need - 256, stream=0)
-    assert rc == sw.SWIGLU_ERR_WORKSPACE
+    rejected_before_launch(
+        lambda: sw.mlp_forward_graph_create(FAKE, FAKE, FAKE, FAKE, 64, 896, 4864, BF16, FAKE,
+                                            need - 256),
+        lambda: sw.mlp_forward(FAKE, FAKE, FAKE, FAKE, 64, 896, 4864, BF16, FAKE, need - 256,
+                               stream=0),
+        sw.SWIGLU_ERR_WORKSPACE)
 
 
 def test_forced_paths():
@@ -195,8 +216,11 @@ def test_mlp_block_arguments_and_workspace():
                need) == sw.SWIGLU_ERR_INVALID_ARG
     assert blk(FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE + 1, FAKE, M, d, dff, BF16, FAKE,
                need) == sw.SWIGLU_ERR_MISALIGNED
-    assert blk(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE,
-               need - 256) == sw.SWIGLU_ERR_WORKSPACE
+    rejected_before_launch(
+        lambda: sw.mlp_block_graph_create(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, M, d, dff,
+                                          BF16, FAKE, need - 256),
+        lambda: blk(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE, need - 256),
+        sw.SWIGLU_ERR_WORKSPACE)
     assert sw.mlp_block_forward_ex(FAKE, FAKE, 1e-5, FAKE, FAKE, None, FAKE, M, d, dff, F32, FAKE,
                                    need, 0, sw.SWIGLU_PATH_WIDE) == sw.SWIGLU_ERR_UNSUPPORTED
 
@@ -259,8 +283,16 @@ def test_workspace_below_the_row_major_plan_is_rejected():
     M, d, dff = 256, 512, 1408
     row_major = _al(M * (-(-dff // 128) * 128) * 2)
     assert sw.swiglu_workspace_bytes(M, d, dff, BF16, 1) > row_major
-    rc = sw.mlp_forward(FAKE, FAKE, FAKE, FAKE, M, d, dff, BF16, FAKE, row_major - 256, stream=0)
-    assert rc == sw.SWIGLU_ERR_WORKSPACE
-    blk = sw.mlp_block_forward(FAKE, FAKE, 1e-6, FAKE, FAKE, None, FAKE, M, d, dff, BF16, FAKE,
-                               _al(M * d * 2) + row_major - 256, stream=0)
-    assert blk == sw.SWIGLU_ERR_WORKSPACE
+    rejected_before_launch(
+        lambda: sw.mlp_forward_graph_create(FAKE, FAKE, FAKE, FAKE, M, d, dff, BF16, FAKE,
+                                            row_major - 256),
+        lambda: sw.mlp_forward(FAKE, FAKE, FAKE, FAKE, M, d, dff, BF16, FAKE, row_major - 256,
+                               stream=0),
+        sw.SWIGLU_ERR_WORKSPACE)
+    blk_bytes = _al(M * d * 2) + row_major - 256
+    rejected_before_launch(
+        lambda: sw.mlp_block_graph_create(FAKE, FAKE, 1e-6, FAKE, FAKE, None, FAKE, M, d, dff,
+                                          BF16, FAKE, blk_bytes),
+        lambda: sw.mlp_block_forward(FAKE, FAKE, 1e-6, FAKE, FAKE, None, FAKE, M, d, dff, BF16,
+                                     FAKE, blk_bytes, stream=0),
+        sw.SWIGLU_ERR_WORKSPACE)
