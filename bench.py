@@ -1,24 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of the fused SwiGLU MLP hot path on one MI355X.
 
-One step = one call of the hot path (swiglu_up / mlp_forward through the C
-ABI) on resident inputs.  The headline line is the 8B-class decode step
+One step = one call of the hot path (swiglu_up, or mlp_forward for the
+workloads with the down projection) through the C ABI, on inputs already
+resident in HBM.  The JSON line's headline is the 8B-class decode step
 (M = 1, d = 4096, d_ff = 14336, bf16) in HBM GB/s of algorithmic traffic
-(both weight matrices once, x once, the output once); the same JSON line also
-carries the 8B-class prefill step (M = 4096) in bf16 TFLOP/s.
+(both weight matrices once, x once, the output once).  The same line carries
+every workload configuration under "configs" (and the quantised-weight decode
+variants under "quantized_decode"), each with its step time, roofline,
+sampled accuracy against the CPU oracle and the oracle's own time on the
+host cores.
 
-Weights are rotated through a ring of copies (>= 1 GB in total) so that the
-256 MB Infinity Cache cannot serve a repeated call: every timed call streams
-its weights from HBM.
+Weights rotate through a ring of copies (>= 1 GiB in total; one copy when a
+copy is larger) so that the 256 MB Infinity Cache cannot serve a repeated
+call: every timed call streams its weights from HBM.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Between workloads (never inside a timed region) the bench launches a tiny
+fill kernel as a marker, three per workload (before set-up, before the first
+step, after the last), so that a rocprofv3 trace or counter run of this
+script can be cut into workloads; `--summarize DIR` turns such runs into the
+summaries under profiles/.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only A,B]
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -31,14 +44,25 @@ import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
-F32_VALU_PEAK_TFLOPS = 157.3
 METRIC = "fused SwiGLU MLP: HBM GB/s at M=1 decode; bf16 TFLOP/s at M=4096 prefill"
-# sources each kernel's recorded counters depend on
+HEADLINE = "decode8b_m1"
+# the workload configurations, in run order
+CONFIGS = ["tiny_decode_f32", "decode8b_m1", "decode8b_m4", "decode8b_m8", "decode8b_m16",
+           "mlp05b_m64", "prefill8b_m4096", "mlp72b_m16", "mlp72b_m2048"]
+QUANT_CONFIGS = ["decode8b_m1_fp8w", "decode8b_m1_mxfp4w", "decode8b_m16_fp8w",
+                 "decode8b_m16_mxfp4w", "mlp72b_m16_fp8w", "mlp72b_m16_mxfp4w"]
+RING_BYTES = 1 << 30
+TOL = {wl.F32: 1e-4, wl.BF16: 2e-2, wl.FP8W: 2e-2, wl.MXFP4W: 2e-2}
+MARKER_ELEMS = 4096
+MARKER_NAME = "FillFunctor"    # torch's fill kernel: the markers' kernel name contains it
+
+# sources each kernel family's code depends on (recorded counters are valid
+# only for the sources they were taken on)
 COMMON_SOURCES = ["geometry.h", "device_common.h", "launch.h", "api.hip"]
-KERNEL_SOURCES = {
-    "skinny_bf16_kernel": COMMON_SOURCES + ["skinny.hip"],
-    "skinny_f32_kernel": COMMON_SOURCES + ["skinny.hip"],
-    "wide_bf16_kernel": COMMON_SOURCES + ["wide.hip", "wide_kernel.h"],
+FAMILY_SOURCES = {
+    "skinny_bf16_kernel": ["skinny.hip"], "skinny_f32_kernel": ["skinny.hip"],
+    "splitk_reduce_kernel": ["skinny.hip"], "wide_bf16_kernel": ["wide.hip", "wide_kernel.h"],
+    "pack_act_kernel": ["pack.hip"], "rmsnorm_kernel": ["norm.hip"],
 }
 
 
@@ -46,38 +70,123 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(kernel: str) -> str:
+def kernel_family(name: str) -> str:
+    """The kernel's unqualified name without template arguments."""
+    base = name.split("(")[0].split("<")[0].strip()
+    return base.split("::")[-1].split()[-1]
+
+
+def sources_hash(kernels) -> str:
+    files = list(COMMON_SOURCES)
+    for k in kernels:
+        for f in FAMILY_SOURCES.get(kernel_family(k), []):
+            if f not in files:
+                files.append(f)
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
+    for f in files:
         with open(os.path.join(ROOT, "gemv_gate_up_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str, kernel: str):
-    """HBM bytes per launch from the committed counter summary, or None when
-    it is missing or was taken on other kernel sources."""
+def traffic_record(workload: str):
+    """The committed counter record of a workload's step, or None when it is
+    missing or was taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel") != kernel or rec.get("src_sha") != kernel_source_hash(kernel):
+    if rec.get("src_sha") != sources_hash(rec.get("kernels", [])):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def weight_ring_copies(w: wl.Workload) -> int:
+    one = 2 * w.d * w.dff * w.weight_bytes + (w.dff * w.d * w.weight_bytes if w.with_down else 0)
+    return max(1, -(-RING_BYTES // int(one))) if one < RING_BYTES else 1
+
+
+def hbm_bound(w: wl.Workload) -> bool:
+    return w.algorithmic_flops() / w.algorithmic_bytes() < \
+        BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+
+def sample_rows(M: int):
+    """Rows the accuracy check compares: every row up to 64, else one row in
+    every 256-row tile (a different offset in each) and the last row."""
+    if M <= 64:
+        return None
+    rows = {min(M - 1, t * 256 + (t * 37) % 256) for t in range(-(-M // 256))}
+    rows.add(M - 1)
+    return sorted(rows)
+
+
+class Inputs:
+    """Seeded inputs, shared by the workloads of one family (same seeds), and
+    the oracle's quantised copies of their weights."""
+
+    def __init__(self):
+        self._fam, self._q = {}, {}
+
+    def get(self, w: wl.Workload) -> dict:
+        key = (w.cfg, w.with_down, w.dtype == wl.F32)
+        if key not in self._fam:
+            t0 = time.time()
+            full = wl.Workload(w.cfg, w.name, w.m_max, w.d, w.dff,
+                               wl.F32 if w.dtype == wl.F32 else wl.BF16, w.with_down, w.m_max)
+            self._fam[key] = wl.make_inputs(full, M=w.m_max)
+            log("inputs for %s generated in %.1fs" % (w.name, time.time() - t0))
+        return self._fam[key]
+
+    def weights_for_oracle(self, w: wl.Workload) -> dict:
+        """Weights as the oracle takes them for this dtype: storage arrays,
+        E4M3 (codes, scales) pairs, or dequantised MXFP4 fp64 arrays."""
+        import oracle
+        inp = self.get(w)
+        names = ("wg", "wu", "wd") if w.with_down else ("wg", "wu")
+        if w.dtype in (wl.F32, wl.BF16):
+            return {k: inp[k] for k in names}
+        key = (w.cfg, w.with_down, w.dtype)
+        if key not in self._q:
+            self._q = {}   # one quantised set at a time (MXFP4 keeps fp64 copies)
+            if w.dtype == wl.FP8W:
+                self._q[key] = {k: oracle.quantize_e4m3(inp[k]) for k in names}
+            else:
+                self._q[key] = {k: oracle.dequantize_mxfp4(*oracle.quantize_mxfp4(inp[k]))
+                                for k in names}
+        return self._q[key]
+
+
+def oracle_call(w: wl.Workload, x: np.ndarray, wts: dict, rows=None, nthreads=0):
+    """The oracle's result of the workload's step on x (fp64)."""
+    import oracle
+    if w.dtype == wl.FP8W:
+        if w.with_down:
+            return oracle.mlp_fp8w(x, *wts["wg"], *wts["wu"], *wts["wd"], rows=rows,
+                                   nthreads=nthreads)
+        return oracle.swiglu_fp8w(x, *wts["wg"], *wts["wu"], rows=rows, nthreads=nthreads)
+    if w.dtype == wl.MXFP4W:
+        x = oracle.to_double(x)
+    if w.with_down:
+        return oracle.mlp(x, wts["wg"], wts["wu"], wts["wd"], rows=rows, nthreads=nthreads)
+    return oracle.swiglu(x, wts["wg"], wts["wu"], rows=rows, nthreads=nthreads)
+
+
+def marker():
+    """A tiny fill kernel that separates workloads in a trace or counter run."""
+    import torch
+    torch.empty(MARKER_ELEMS, dtype=torch.float32, device="cuda").fill_(1.0)
 
 
 class Runner:
     """Device buffers and the C-ABI call for one workload."""
 
-    def __init__(self, w: wl.Workload, copies: int, path: int = 0, graph: bool = False,
-                 block: bool = False):
+    def __init__(self, w: wl.Workload, inp: dict, copies: int, path: int = 0,
+                 graph: bool = False, block: bool = False):
         import torch
         import gemv_gate_up_amd as sw
         self.torch, self.sw, self.w = torch, sw, w
-        t0 = time.time()
-        self.inp = wl.make_inputs(w, M=w.M)
-        log("inputs for %s generated in %.1fs" % (w.name, time.time() - t0))
         tdt = torch.float32 if w.dtype == wl.F32 else torch.int16
 
         def dev(a):
@@ -86,17 +195,17 @@ class Runner:
                 a = a.view(np.int16)
             return torch.from_numpy(a).to("cuda")
 
-        self.x = dev(self.inp["x"])
+        self.x = dev(inp["x"][:w.M])
         wp = torch.empty(sw.swiglu_packed_bytes(w.d, w.dff, w.dtype), dtype=torch.uint8,
                          device="cuda")
-        sw.check(sw.swiglu_pack_weights(dev(self.inp["wg"]), dev(self.inp["wu"]), wp, w.d, w.dff,
+        sw.check(sw.swiglu_pack_weights(dev(inp["wg"]), dev(inp["wu"]), wp, w.d, w.dff,
                                         w.dtype), "pack")
         self.wps = [wp] + [wp.clone() for _ in range(copies - 1)]
         self.wdps = [None] * copies
         if w.with_down:
             wdp = torch.empty(sw.swiglu_down_packed_bytes(w.d, w.dff, w.dtype), dtype=torch.uint8,
                               device="cuda")
-            sw.check(sw.swiglu_pack_down(dev(self.inp["wd"]), wdp, w.d, w.dff, w.dtype), "pack")
+            sw.check(sw.swiglu_pack_down(dev(inp["wd"]), wdp, w.d, w.dff, w.dtype), "pack")
             self.wdps = [wdp] + [wdp.clone() for _ in range(copies - 1)]
         ncols = w.d if w.with_down else w.dff
         self.out = torch.empty((w.M, ncols), dtype=tdt, device="cuda")
@@ -112,8 +221,6 @@ class Runner:
         else:
             self.ws_bytes = sw.swiglu_workspace_bytes_ex(w.M, w.d, w.dff, w.dtype,
                                                          int(w.with_down), path)
-        if self.ws_bytes < 0:
-            raise RuntimeError("path %d: %s" % (path, sw.swiglu_status_string(self.ws_bytes)))
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream()
@@ -152,26 +259,20 @@ class Runner:
                                               self.sh, self.req_path)
         elif self.graphs:
             rc = sw._lib.swiglu_graph_launch(self.graphs[i % self.copies], self.sh)
-        elif self.req_path and w.with_down:
+        elif w.with_down:
             rc = sw._lib.mlp_forward_ex(xp, wpp, wdpp, self.out.data_ptr(), w.M, w.d, w.dff,
                                         w.dtype, self.ws.data_ptr(), self.ws_bytes, self.sh,
                                         self.req_path)
-        elif self.req_path:
+        else:
             rc = sw._lib.swiglu_up_ex(xp, wpp, self.out.data_ptr(), w.M, w.d, w.dff, w.dtype,
                                       self.ws.data_ptr(), self.ws_bytes, self.sh, self.req_path)
-        elif w.with_down:
-            rc = sw._lib.mlp_forward(xp, wpp, wdpp, self.out.data_ptr(), w.M, w.d, w.dff, w.dtype,
-                                     self.ws.data_ptr(), self.ws_bytes, self.sh)
-        else:
-            rc = sw._lib.swiglu_up(xp, wpp, self.out.data_ptr(), w.M, w.d, w.dff, w.dtype,
-                                   self.ws.data_ptr(), self.ws_bytes, self.sh)
         if rc != 0:
             raise RuntimeError("step failed: %s" % sw.swiglu_status_string(rc))
 
     def time(self, steps: int, warmup: int) -> dict:
         """K back-to-back steps between two synchronisations: the host clock
         gives the step rate, and a pair of HIP events recorded on the launch
-        stream around the same K launches gives the device time per launch."""
+        stream around the same K steps gives the device time per step."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
@@ -186,7 +287,15 @@ class Runner:
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         return {"wall_ms_per_step": (t1 - t0) * 1e3 / steps,
-                "event_ms_per_launch": e0.elapsed_time(e1) / steps}
+                "event_ms_per_step": e0.elapsed_time(e1) / steps}
+
+    def result(self, rows=None) -> np.ndarray:
+        """The last step's output (all weight copies are equal) as fp64."""
+        o = self.out if rows is None else self.out[rows]
+        a = o.cpu().numpy()
+        if self.w.dtype != wl.F32:
+            return wl.bf16_bits_to_f32(a.view(np.uint16)).astype(np.float64)
+        return a.astype(np.float64)
 
 
 PATHS = {"auto": 0, "skinny": 1, "wide": 2, "phased": 3}
@@ -205,129 +314,323 @@ def block_bytes(w: wl.Workload) -> int:
     return w.algorithmic_bytes() + 2 * w.d * w.elem_bytes
 
 
-def measure(w: wl.Workload, steps: int, warmup: int, copies: int, path: int = 0,
-            graph: bool = False, block: bool = False) -> dict:
-    r = Runner(w, copies, path, graph, block)
-    t = r.time(steps, warmup)
-    kern = dominant_kernel(w, r.path)
-    per_launch_ms = t["event_ms_per_launch"]
-    single_kernel = (not w.with_down) and (
-        r.path in (2, 3) or r.sw.swiglu_workspace_bytes(w.M, w.d, w.dff, w.dtype, 0) == 0)
-    res = {"runner": r, "timing": t, "kernel": kern, "path": r.path,
-           "single_kernel_step": single_kernel}
-    bytes_alg = block_bytes(w) if block else w.algorithmic_bytes()
-    flops_alg = w.algorithmic_flops()
-    hbm_bound = flops_alg / bytes_alg < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if hbm_bound:
-        achieved = bytes_alg / (per_launch_ms * 1e-3) / 1e9
-        res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = flops_alg / (per_launch_ms * 1e-3) / 1e12
-        res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1),
-                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-    # recorded counters are for the dispatcher's own path
-    res["roofline"]["traffic"] = (traffic_from_profile(w.name, kern)
-                                  if not (path or graph or block) else None)
-    res["roofline"]["kernel"] = kern
-    res["roofline"]["kernel_ms"] = round(per_launch_ms, 5)
-    if r.path in (2, 3) and not (w.with_down or block or graph):
-        # with the reported workspace the many-rows step packs x first; the
-        # events span both launches
-        res["roofline"]["step_kernels"] = ["pack_act_kernel", kern]
-    return res
+def accuracy(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> dict:
+    """Pass/fail under |gpu - ref| <= tol (1 + |ref|), with the diagnostics:
+    max error, max scaled error, and the share of elements off by more than
+    1% of |ref| (elements with |ref| > 1e-3)."""
+    err = np.abs(got - ref)
+    scaled = err / (1.0 + np.abs(ref))
+    big = np.abs(ref) > 1e-3
+    rel = np.where(big, err / np.maximum(np.abs(ref), 1e-300), 0.0)
+    return {"checked": what, "elements": int(got.size), "tol": tol,
+            "ok": bool(np.all(np.isfinite(got)) and np.all(scaled <= tol)),
+            "max_abs": float(err.max()), "max_scaled": float(scaled.max()),
+            "frac_rel_gt_1pct": float((rel > 0.01).sum() / max(1, big.sum()))}
 
 
-def cpu_baseline(w: wl.Workload, inp: dict, budget_s: float) -> dict:
-    """The oracle, as it stands, on the host cores: full workload calls
-    repeated for about budget_s seconds (at least one)."""
-    import oracle
-    threads = oracle.available_cores()
-    x = inp["x"][:w.M]
-    if w.dtype == wl.FP8W:   # quantised once, outside the timing
-        q = {k: oracle.quantize_e4m3(inp[k]) for k in ("wg", "wu", "wd") if k in inp}
-    if w.dtype == wl.MXFP4W:
-        q = {k: oracle.dequantize_mxfp4(*oracle.quantize_mxfp4(inp[k]))
-             for k in ("wg", "wu", "wd") if k in inp}
-        x = oracle.to_double(x)
+def cpu_baseline(w: wl.Workload, inputs: Inputs, budget_s: float, nthreads: int) -> dict:
+    """The oracle, as it stands, on `nthreads` host cores: the workload's full
+    step repeated for about budget_s (at least once); above 64 rows a
+    contiguous block of 16 rows is timed instead and scaled linearly to M.
+    Reported in the workload's unit."""
+    inp = inputs.get(w)
+    wts = inputs.weights_for_oracle(w)
+    rows_timed = w.M if w.M <= 64 else 16
+    x = inp["x"][:rows_timed]
     reps, t0 = 0, time.perf_counter()
     while True:
-        if w.dtype == wl.MXFP4W and w.with_down:
-            oracle.mlp(x, q["wg"], q["wu"], q["wd"], nthreads=threads)
-        elif w.dtype == wl.MXFP4W:
-            oracle.swiglu(x, q["wg"], q["wu"], nthreads=threads)
-        elif w.dtype == wl.FP8W and w.with_down:
-            oracle.mlp_fp8w(x, *q["wg"], *q["wu"], *q["wd"], nthreads=threads)
-        elif w.dtype == wl.FP8W:
-            oracle.swiglu_fp8w(x, *q["wg"], *q["wu"], nthreads=threads)
-        elif w.with_down:
-            oracle.mlp(x, inp["wg"], inp["wu"], inp["wd"], nthreads=threads)
-        else:
-            oracle.swiglu(x, inp["wg"], inp["wu"], nthreads=threads)
+        oracle_call(w, x, wts, nthreads=nthreads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    per_call = el / reps
-    return {"value": round(w.algorithmic_bytes() / per_call / 1e9, 3), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": "%d full %s call(s) (M=%d, d=%d, dff=%d) in %.1f s wall, fp64" % (
-                reps, w.name, w.M, w.d, w.dff, el),
-            "ms_per_call": round(per_call * 1e3, 2)}
+    per_call = el / reps * (w.M / rows_timed)
+    if hbm_bound(w):
+        value, unit = w.algorithmic_bytes() / per_call / 1e9, "GB/s"
+    else:
+        value, unit = w.algorithmic_flops() / per_call / 1e12, "TFLOP/s"
+    if rows_timed == w.M:
+        sample = "%d full %s call(s) (M=%d, d=%d, dff=%d) in %.1f s wall, fp64" % (
+            reps, w.name, w.M, w.d, w.dff, el)
+    else:
+        sample = ("%d call(s) on rows 0-%d of %s (d=%d, dff=%d) in %.1f s wall, fp64, "
+                  "scaled linearly to M=%d" % (reps, rows_timed - 1, w.name, w.d, w.dff, el, w.M))
+    return {"value": round(value, 4), "unit": unit, "cores": nthreads, "kind": "oracle",
+            "sample": sample, "ms_per_call": round(per_call * 1e3, 3)}
 
 
-def probe() -> int:
+def measure(w: wl.Workload, inputs: Inputs, steps: int, warmup: int, copies: int,
+            path: int = 0, graph: bool = False, block: bool = False,
+            check: bool = True) -> dict:
+    """Times one workload; returns its record (and the runner, closed)."""
+    marker()
+    r = Runner(w, inputs.get(w), copies, path, graph, block)
+    marker()
+    t = r.time(steps, warmup)
+    marker()
+    bytes_alg = block_bytes(w) if block else w.algorithmic_bytes()
+    flops_alg = w.algorithmic_flops()
+    ms = t["event_ms_per_step"]
+    kern = dominant_kernel(w, r.path)
+    if hbm_bound(w):
+        achieved = bytes_alg / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        value, unit = bytes_alg / (t["wall_ms_per_step"] * 1e-3) / 1e9, "GB/s"
+    else:
+        achieved = flops_alg / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        value, unit = flops_alg / (t["wall_ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
+    # recorded counters are for the dispatcher's own path with the reported workspace
+    rec = traffic_record(w.name) if not (path or graph or block) else None
+    roof["traffic"] = rec["hbm_bytes_per_step"] if rec else None
+    roof["kernel"] = kern
+    roof["step_kernels"] = rec["kernels"] if rec else None
+    roof["event_ms_per_step"] = round(ms, 5)
+    out = {"workload": w.name, "M": w.M, "d": w.d, "dff": w.dff,
+           "dtype": wl.DTYPE_NAMES[w.dtype], "with_down": w.with_down,
+           "path": PATH_NAMES[r.path], "weight_copies": copies, "steps": steps, "warmup": warmup,
+           "value": round(value, 3 if unit == "TFLOP/s" else 1), "unit": unit,
+           "ms_per_step": round(t["wall_ms_per_step"], 5),
+           "algorithmic_bytes": bytes_alg, "algorithmic_flops": flops_alg,
+           "roofline": roof, "timing_ms": {k: round(v, 5) for k, v in t.items()}}
+    if check and not block:
+        rows = sample_rows(w.M)
+        got = r.result(rows)
+        inp = inputs.get(w)
+        ref = oracle_call(w, inp["x"][:w.M], inputs.weights_for_oracle(w), rows=rows)
+        what = ("every output" if rows is None else
+                "%d whole rows (one per 256-row tile and the last)" % len(rows))
+        out["accuracy"] = accuracy(got, ref, TOL[w.dtype], what)
+    r.close()
+    return out
+
+
+def run_order(only):
+    names = CONFIGS + QUANT_CONFIGS
+    return [n for n in names if n in only] if only else names
+
+
+def probe(order) -> int:
     """Kernels for hardware-counter runs: a plain copy of known size (reads
-    and writes exactly 1 GiB) to calibrate FETCH_SIZE / WRITE_SIZE, then the
-    decode (bf16, FP8 and MXFP4 weights) and prefill steps as the bench runs them."""
+    and writes exactly 1 GiB) to calibrate FETCH_SIZE / WRITE_SIZE, then
+    a few steps of each workload as the bench runs them (with its markers);
+    prints no timing."""
     import torch
+    print(json.dumps({"probe_order": order}), flush=True)
     n = 1 << 30
-    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")   # no fill: a fill is a marker
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
     torch.cuda.empty_cache()
-    for name, steps in (("decode8b_m1", 5), ("decode8b_m1_fp8w", 5), ("decode8b_m1_mxfp4w", 5),
-                        ("prefill8b_m4096", 3)):
+    inputs = Inputs()
+    for name in order:
         w = wl.WORKLOADS[name]
-        r = Runner(w, 5 if w.M == 1 else 1)
-        for i in range(steps):
+        marker()
+        r = Runner(w, inputs.get(w), weight_ring_copies(w))
+        marker()
+        for i in range(5):
             r.step(i)
+        marker()
         torch.cuda.synchronize()
+        r.close()
         del r
         torch.cuda.empty_cache()
     log("probe done")
     return 0
 
 
+# ---------------------------------------------------------------- profiles
+def _segments(names):
+    """Cuts a dispatch sequence at the bench's markers: for each workload,
+    the dispatches between its second and third marker (its steps)."""
+    idx = [i for i, n in enumerate(names) if MARKER_NAME in n]
+    if len(idx) % 3:
+        raise ValueError("marker count %d is not a multiple of 3" % len(idx))
+    return [(idx[3 * j + 1] + 1, idx[3 * j + 2]) for j in range(len(idx) // 3)]
+
+
+def _step_kernels(names, nsteps):
+    """Kernel names of one step, from a run of nsteps identical steps."""
+    if not names or len(names) % nsteps:
+        raise ValueError("%d dispatches do not split into %d steps" % (len(names), nsteps))
+    k = len(names) // nsteps
+    step = names[:k]
+    if names != step * nsteps:
+        raise ValueError("steps do not repeat the same kernels")
+    return step
+
+
+def _read_csv(pattern):
+    files = glob.glob(pattern, recursive=True)
+    if not files:
+        raise FileNotFoundError(pattern)
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_per_step(rows, order, nsteps=5):
+    """Per workload: (step kernel names, counter KiB per kernel of a step,
+    averaged over the steps), plus the calibration copy's mean."""
+    rows = sorted(rows, key=lambda x: int(x["Dispatch_Id"]))
+    names = [r["Kernel_Name"] for r in rows]
+    vals = [float(r["Counter_Value"]) for r in rows]
+    cal = [v for n, v, r in zip(names, vals, rows)
+           if "copyBuffer" in n and int(r["Grid_Size"]) == 131072][:3]
+    if len(cal) != 3:
+        raise ValueError("calibration copies not found")
+    out = {}
+    for name, (a, b) in zip(order, _segments(names)):
+        step = _step_kernels(names[a:b], nsteps)
+        k = len(step)
+        per = [statistics.mean(vals[a + j::k][:nsteps]) for j in range(k)]
+        out[name] = (step, per)
+    return out, statistics.mean(cal)
+
+
+def summarize(d: str) -> int:
+    """Writes profiles/traffic_<workload>.json and profiles/<kernel>-<workload>.md
+    from a directory of rocprofv3 runs of this script:
+      d/trace/**/*kernel_trace.csv   --kernel-trace --stats of the default bench run
+      d/trace_bench.log              that run's stdout (the JSON line)
+      d/fetch/**/*counter_collection.csv, d/write/...   --pmc FETCH_SIZE / WRITE_SIZE of --probe
+    """
+    bench_line = json.loads([ln for ln in open(os.path.join(d, "trace_bench.log"))
+                             if ln.startswith("{")][-1])
+    order = bench_line["order"]
+    recs = dict(bench_line["configs"])
+    recs.update(bench_line.get("quantized_decode", {}))
+    tr = _read_csv(os.path.join(d, "trace", "**", "*kernel_trace.csv"))
+    tr.sort(key=lambda x: int(x["Start_Timestamp"]))
+    tnames = [x["Kernel_Name"] for x in tr]
+    fetch_rows = _read_csv(os.path.join(d, "fetch", "**", "*counter_collection.csv"))
+    write_rows = _read_csv(os.path.join(d, "write", "**", "*counter_collection.csv"))
+    porder = json.loads([ln for ln in open(os.path.join(d, "fetch.log"))
+                         if ln.startswith('{"probe_order"')][0])["probe_order"]
+    fetch, fcal = _counter_per_step(fetch_rows, porder)
+    write, wcal = _counter_per_step(write_rows, porder)
+    ff, wf = (1 << 20) / fcal, (1 << 20) / wcal
+    trace_cmd = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace "
+                 "-o bench -- python3 <repo>/bench.py --no-cpu")
+    pmc_cmd = ("cd /tmp && rocprofv3 --pmc %s --output-format csv -d <out>/%s -o probe -- "
+               "python3 <repo>/bench.py --probe")
+    for name, (a, b) in zip(order, _segments(tnames)):
+        rec = recs[name]
+        steps = rec["steps"]
+        disp = tr[a:b]
+        step = _step_kernels([x["Kernel_Name"] for x in disp], steps + rec["warmup"])
+        k = len(step)
+        timed = disp[len(disp) - k * steps:]
+        durs = [[(int(x["End_Timestamp"]) - int(x["Start_Timestamp"])) for x in timed[j::k]]
+                for j in range(k)]
+        span = (int(timed[-1]["End_Timestamp"]) - int(timed[0]["Start_Timestamp"])) / steps
+        fstep, fper = fetch[name]
+        wstep, wper = write[name]
+        if [kernel_family(s) for s in fstep] != [kernel_family(s) for s in step] or \
+                [kernel_family(s) for s in wstep] != [kernel_family(s) for s in step]:
+            raise ValueError("%s: the counter runs launched other kernels" % name)
+        fb = [round(v * 1024 * ff) for v in fper]
+        wb = [round(v * 1024 * wf) for v in wper]
+        total = sum(fb) + sum(wb)
+        alg = rec["algorithmic_bytes"]
+        sha = sources_hash(step)
+        traffic = {"workload": name, "src_sha": sha, "kernels": [kernel_family(s) for s in step],
+                   "kernel_names": step, "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+                   "fetch_kib_raw": [round(v, 1) for v in fper],
+                   "write_kib_raw": [round(v, 1) for v in wper],
+                   "hbm_bytes_per_step": total, "algorithmic_bytes": alg,
+                   "ratio": round(total / alg, 3)}
+        with open(os.path.join(ROOT, "profiles", "traffic_%s.json" % name), "w") as f:
+            json.dump(traffic, f, indent=1)
+            f.write("\n")
+        dom = rec["roofline"]["kernel"]
+        rows = []
+        for j, s in enumerate(step):
+            dj = durs[j]
+            rows.append("| %d | `%s` | %d | %.0f | %d | %d | %d | %d |" % (
+                j + 1, s[:110], len(dj), statistics.mean(dj), min(dj), max(dj), fb[j], wb[j]))
+        ksum = sum(statistics.mean(dj) for dj in durs) / 1e3
+        rl = rec["roofline"]
+        md = "\n".join([
+            "# %s: %s (MI355X, gfx950)" % (name, ", ".join(kernel_family(s) for s in step)),
+            "",
+            "Kernel sources sha256[:16] = `%s` (bench.py `sources_hash` over this step's "
+            "kernels). %s steps of M=%d, d=%d, dff=%d (%s, %s), %d timed after %d warmup, "
+            "weights rotated over %d copies." % (sha, "MLP" if rec["with_down"] else "swiglu_up",
+                                                 rec["M"], rec["d"], rec["dff"], rec["dtype"],
+                                                 rec["path"], steps, rec["warmup"],
+                                                 rec["weight_copies"]),
+            "",
+            "Kernel trace: `%s`" % trace_cmd,
+            "",
+            "HBM counters: `%s` and the same with `WRITE_SIZE` (`<out>/write`)."
+            % (pmc_cmd % ("FETCH_SIZE", "fetch")),
+            "",
+            "Per kernel of one step, over the %d timed steps only (trace), and its HBM bytes per "
+            "launch (counters, mean of 5 probe steps; fetch x %.4f, write x %.4f from a 1 GiB "
+            "copy):" % (steps, ff, wf),
+            "",
+            "| # | kernel | launches | average ns | min ns | max ns | fetch B | write B |",
+            "|---|---|---|---|---|---|---|---|",
+        ] + rows + [
+            "",
+            "Sum of the kernel averages: %.2f us per step; first start to last end over the "
+            "timed steps: %.2f us per step. bench.py in the same run (HIP events on the launch "
+            "stream around the same steps): %.2f us per step, roofline frac %.4f of %s %s." % (
+                ksum, span / 1e3, rl["event_ms_per_step"] * 1e3, rl["frac"], rl["peak"],
+                rl["unit"]),
+            "",
+            "HBM traffic per step: fetch %d B + write %d B = **%d B** against %d algorithmic "
+            "bytes (ratio %.2f)." % (sum(fb), sum(wb), total, alg, total / alg),
+            ""])
+        fn = os.path.join(ROOT, "profiles", "%s-%s.md" % (dom, name))
+        with open(fn, "w") as f:
+            f.write(md)
+        log("wrote", fn)
+    return 0
+
+
+# ---------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200,
+                    help="timed steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode8b_m1", choices=sorted(wl.WORKLOADS))
-    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--config-steps", type=int, default=100,
+                    help="timed steps of the other decode-regime workloads (at least --steps)")
+    ap.add_argument("--prefill-steps", type=int, default=20,
+                    help="timed steps of the compute-bound workloads")
     ap.add_argument("--prefill-warmup", type=int, default=40,
-                    help="untimed prefill steps first: the clock needs ~30 ms of matrix work to settle")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-variants", action="store_true",
-                    help="skip the FP8- and MXFP4-weight decode lines")
+                    help="their untimed steps first: the clock needs ~30 ms of matrix work "
+                         "to settle")
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(wl.WORKLOADS),
+                    help="headline workload (the configs are still all run unless --only)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated workloads to run besides the headline (default: all)")
     ap.add_argument("--block", action="store_true",
-                    help="time the MLP block (RMSNorm, MLP, bias and residual) on a workload "
-                         "with the down projection")
+                    help="time the MLP block (RMSNorm, MLP, bias and residual) on the headline "
+                         "workload, which needs the down projection; no configs")
     ap.add_argument("--graph", action="store_true",
-                    help="replay recorded calls (HIP graphs) instead of direct calls")
+                    help="replay recorded calls (HIP graphs) on the headline workload; no configs")
     ap.add_argument("--path", default="auto", choices=sorted(PATHS),
-                    help="force a kernel path for the main workload (default: the dispatcher's)")
+                    help="force a kernel path for the headline workload; no configs")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="oracle time budget of the headline's CPU baseline")
+    ap.add_argument("--config-cpu-seconds", type=float, default=1.5)
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection run: a 1 GiB device copy (calibration), then a few "
-                         "steps of the decode and prefill workloads; prints no timing")
+                         "steps of every workload; prints no timing")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write profiles/ from rocprofv3 runs of this script in DIR (no GPU)")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args.summarize)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(one GPU's share of a sharded MLP is the same kernel at a smaller d_ff).",
@@ -336,72 +639,89 @@ def main() -> int:
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    only = [s for s in args.only.split(",") if s]
+    for s in only:
+        if s not in wl.WORKLOADS:
+            ap.error("unknown workload %s" % s)
+    order = run_order(only)
     if args.probe:
-        return probe()
-    w = wl.WORKLOADS[args.workload]
-    one_copy = int(2 * w.d * w.dff * w.weight_bytes)
-    copies = max(1, -(-(1 << 30) // one_copy)) if one_copy < (1 << 30) else 1
-    log("workload %s: %s, %d weight copies" % (w.name, w, copies))
-    m = measure(w, args.steps, args.warmup, copies, PATHS[args.path], args.graph, args.block)
-    t = m["timing"]
-    alg_bytes = block_bytes(w) if args.block else w.algorithmic_bytes()
-    value_bytes = alg_bytes / (t["wall_ms_per_step"] * 1e-3) / 1e9
+        return probe(order)
+    import oracle
+    cores = oracle.available_cores()
+    inputs = Inputs()
+    hw = wl.WORKLOADS[args.workload]
+    special = args.block or args.graph or args.path != "auto"
+
+    def steps_of(w):
+        if w.name == hw.name:
+            return args.steps, args.warmup
+        if hbm_bound(w):
+            return max(args.steps, args.config_steps), max(args.warmup, 20)
+        return args.prefill_steps, args.prefill_warmup
+
+    def run(w, headline=False):
+        steps, warmup = steps_of(w)
+        copies = weight_ring_copies(w)
+        log("workload %s: %s, %d weight copies" % (w.name, w, copies))
+        rec = measure(w, inputs, steps, warmup, copies,
+                      PATHS[args.path] if headline else 0, args.graph and headline,
+                      args.block and headline)
+        torch.cuda.empty_cache()
+        if not args.no_cpu:
+            budget = args.cpu_seconds if headline else args.config_cpu_seconds
+            rec["cpu_baseline"] = cpu_baseline(w, inputs, budget, cores)
+            if w.name in ("tiny_decode_f32", "decode8b_m1") and not special:
+                rec["cpu_baseline"]["single_thread"] = cpu_baseline(w, inputs, 2.0, 1)
+        return rec
+
+    configs, quant = {}, {}
+    run_names = [] if special else [n for n in order if n != hw.name]
+    # the headline runs first when it is not one of the configs
+    head = run(hw, headline=True)
+    executed = [hw.name]
+    for name in run_names:
+        w = wl.WORKLOADS[name]
+        (quant if name in QUANT_CONFIGS else configs)[name] = run(w)
+        executed.append(name)
+    if hw.name in CONFIGS and not special:
+        configs[hw.name] = head
+    elif hw.name in QUANT_CONFIGS and not special:
+        quant[hw.name] = head
+    headline_value = head["value"]
     rec = {
         "metric": METRIC,
-        "value": round(value_bytes, 1),
-        "unit": "GB/s",
+        "value": headline_value,
+        "unit": head["unit"],
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(t["wall_ms_per_step"], 5),
+        "steps": head["steps"],
+        "warmup": head["warmup"],
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.DTYPE_NAMES[w.dtype],
+        "dtype": head["dtype"],
         "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights, bf16 RNE)",
-        "config": {"workload": w.name, "M": w.M, "d": w.d, "dff": w.dff,
-                   "with_down": w.with_down, "path": PATH_NAMES[m["path"]],
-                   "weight_copies": copies, "graph": bool(args.graph), "block": bool(args.block),
-                   "algorithmic_bytes": alg_bytes,
-                   "algorithmic_flops": w.algorithmic_flops()},
-        "roofline": m["roofline"],
-        "timing_ms": {k: round(v, 5) for k, v in t.items()},
+        "config": {"workload": hw.name, "M": hw.M, "d": hw.d, "dff": hw.dff,
+                   "with_down": hw.with_down, "path": head["path"],
+                   "weight_copies": head["weight_copies"], "graph": bool(args.graph),
+                   "block": bool(args.block), "algorithmic_bytes": head["algorithmic_bytes"],
+                   "algorithmic_flops": head["algorithmic_flops"]},
+        "roofline": head["roofline"],
+        "timing_ms": head["timing_ms"],
     }
-    if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, m["runner"].inp, args.cpu_seconds)
-    m["runner"].close()
-    del m
-    torch.cuda.empty_cache()
-    if not args.no_variants and w.name == "decode8b_m1":
-        # the same decode step with quantised weights (packed from the same
-        # bf16 weights); reported beside the bf16 headline, never as it
-        rec["quantized_decode"] = {}
-        for name in ("decode8b_m1_fp8w", "decode8b_m1_mxfp4w"):
-            q = wl.WORKLOADS[name]
-            qcopies = max(1, -(-(1 << 30) // int(2 * q.d * q.dff * q.weight_bytes)))
-            mq = measure(q, args.steps, args.warmup, qcopies)
-            tq = mq["timing"]
-            rec["quantized_decode"][name] = {
-                "dtype": wl.DTYPE_NAMES[q.dtype],
-                "value": round(q.algorithmic_bytes() / (tq["wall_ms_per_step"] * 1e-3) / 1e9, 1),
-                "unit": "GB/s", "ms_per_step": round(tq["wall_ms_per_step"], 5),
-                "algorithmic_bytes": q.algorithmic_bytes(), "roofline": mq["roofline"],
-                "timing_ms": {k: round(v, 5) for k, v in tq.items()},
-            }
-            mq["runner"].close()
-            del mq
-            torch.cuda.empty_cache()
-    if not args.no_prefill and w.name != "prefill8b_m4096":
-        p = wl.WORKLOADS["prefill8b_m4096"]
-        mp = measure(p, args.prefill_steps, args.prefill_warmup, 1)
-        tp = mp["timing"]
-        rec["prefill"] = {
-            "workload": p.name, "M": p.M, "d": p.d, "dff": p.dff,
-            "value": round(p.algorithmic_flops() / (tp["wall_ms_per_step"] * 1e-3) / 1e12, 1),
-            "unit": "TFLOP/s", "ms_per_step": round(tp["wall_ms_per_step"], 4),
-            "steps": args.prefill_steps, "warmup": args.prefill_warmup, "roofline": mp["roofline"],
-            "timing_ms": {k: round(v, 5) for k, v in tp.items()},
-        }
+    if "accuracy" in head:
+        rec["accuracy"] = head["accuracy"]
+    if "cpu_baseline" in head:
+        rec["cpu_baseline"] = head["cpu_baseline"]
+    if "prefill8b_m4096" in configs:
+        p = configs["prefill8b_m4096"]
+        rec["prefill"] = {k: p[k] for k in ("workload", "M", "d", "dff", "value", "unit",
+                                            "ms_per_step", "steps", "warmup", "roofline")}
+    if configs:
+        rec["configs"] = configs
+    if quant:
+        rec["quantized_decode"] = quant
+    rec["order"] = executed
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -28,9 +28,15 @@ def _inputs(name):
 
 
 def _rows(M):
+    """All rows up to 64; else whole rows spread over the output: one in every
+    256-row tile (a different offset in each), the first and last rows of
+    the last (possibly ragged) tile, and the rows next to the 128-row and
+    256-row tile boundaries."""
     if M <= 64:
         return None                    # all rows
     cand = [0, 1, 127, 128, 255, 256, M // 2 + 3, M - 257, M - 2, M - 1]
+    cand += [t * 256 + (t * 37 + 11) % 256 for t in range(-(-M // 256))]
+    cand += [(M - 1) // 256 * 256]
     return sorted({r for r in cand if 0 <= r < M})
 
 
