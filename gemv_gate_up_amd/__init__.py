@@ -31,6 +31,8 @@ SWIGLU_ERR_UNSUPPORTED = -2
 SWIGLU_ERR_MISALIGNED = -3
 SWIGLU_ERR_WORKSPACE = -4
 SWIGLU_ERR_HIP = -5
+SWIGLU_ERR_SCRATCH = -6
+SWIGLU_SCRATCH_BYTES = 32 << 20
 
 SWIGLU_PATH_AUTO = 0
 SWIGLU_PATH_SKINNY = 1
@@ -75,6 +77,7 @@ _SIGS = {
     "swiglu_pack_down": (_int, [_vp, _vp, _i64, _i64, _int, _vp]),
     "swiglu_up": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
     "swiglu_up_ex": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _vp, _int]),
+    "swiglu_up_noalloc": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp]),
     "mlp_forward": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
     "mlp_forward_ex": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _vp, _int]),
     "swiglu_up_graph_create": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _sz, _int,
@@ -169,6 +172,11 @@ def swiglu_up_ex(x, Wpacked, out, M, d, dff, dtype, workspace=None, workspace_by
                  stream=None, path=SWIGLU_PATH_AUTO) -> int:
     return _lib.swiglu_up_ex(_ptr(x), _ptr(Wpacked), _ptr(out), M, d, dff, dtype,
                              _ptr(workspace), workspace_bytes, _stream(stream), path)
+
+
+def swiglu_up_noalloc(x, Wpacked, out, M, d, dff, dtype, stream=None) -> int:
+    return _lib.swiglu_up_noalloc(_ptr(x), _ptr(Wpacked), _ptr(out), M, d, dff, dtype,
+                                  _stream(stream))
 
 
 def mlp_forward(x, Wpacked, Wdpacked, y, M, d, dff, dtype, workspace=None, workspace_bytes=0,

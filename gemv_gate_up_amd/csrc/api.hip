@@ -11,6 +11,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "launch.h"
@@ -389,6 +391,70 @@ int record_graph(Call&& call, swiglu_graph_t* out)
     return SWIGLU_OK;
 }
 
+// ---- the entry point that allocates nothing (swiglu_up_noalloc)
+// Its workspace is this fixed array: every GPU the library runs on holds a
+// copy of it until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: the array's address on a device
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to kernels.
+constexpr size_t SCRATCH_BYTES = SWIGLU_SCRATCH_BYTES;
+constexpr int MAX_DEVICES = 64;
+static_assert(SCRATCH_BYTES % WS_ALIGN == 0, "whole allocation units");
+
+__device__ __attribute__((aligned(256))) uint8_t scratch[SCRATCH_BYTES];
+
+std::atomic<void*> scratch_addr[MAX_DEVICES];
+std::mutex scratch_mutex;
+
+// The device address of the current device's copy of the array, looked up
+// on the device's first call and kept.
+int scratch_address(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return SWIGLU_ERR_HIP;
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return SWIGLU_ERR_UNSUPPORTED;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mutex);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return SWIGLU_ERR_HIP;
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SWIGLU_OK;
+}
+
+// swiglu_up on the automatic path with the array as its workspace: the
+// packed plan when packed x fits, else x read in place; split-K partials
+// always fit (at most 16 MiB for any shape within the limits).  The
+// arguments and the plan are checked first, without any HIP call; a plan
+// that needs more than the array is SWIGLU_ERR_SCRATCH.  Nothing in the
+// array needs to start at zero: the kernels write every byte they read
+// (partials, and packed x with its zero padding) earlier in the same call.
+int do_up_noalloc(const void* x, const void* wp, void* out, int64_t M, int64_t d, int64_t dff,
+                  int dtype, hipStream_t s)
+{
+    // a placeholder address (aligned, never dereferenced) while validating
+    void* const placeholder = (void*)(uintptr_t)WS_ALIGN;
+    int rc = do_up(x, wp, out, M, d, dff, dtype, placeholder, SCRATCH_BYTES, s, SWIGLU_PATH_AUTO,
+                   false);
+    if (rc == SWIGLU_ERR_WORKSPACE)
+        return SWIGLU_ERR_SCRATCH;
+    if (rc != SWIGLU_OK || M == 0)
+        return rc;
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != SWIGLU_OK)
+        return rc;
+    rc = do_up(x, wp, out, M, d, dff, dtype, ws, SCRATCH_BYTES, s, SWIGLU_PATH_AUTO);
+    return rc == SWIGLU_ERR_WORKSPACE ? SWIGLU_ERR_SCRATCH : rc;
+}
+
 int do_pack(const void* src0, const void* src1, void* dst, const PackGeom& g, int plain,
             hipStream_t s)
 {
@@ -412,6 +478,7 @@ const char* swiglu_status_string(int status)
     case SWIGLU_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
     case SWIGLU_ERR_WORKSPACE: return "workspace too small";
     case SWIGLU_ERR_HIP: return "HIP launch error";
+    case SWIGLU_ERR_SCRATCH: return "call needs more than the fixed scratch array";
     default: return "unknown status";
     }
 }
@@ -491,6 +558,12 @@ int swiglu_up_ex(const void* x, const void* Wpacked, void* out, int64_t M, int64
                  int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream, int path)
 {
     return do_up(x, Wpacked, out, M, d, dff, dtype, workspace, workspace_bytes, stream, path);
+}
+
+int swiglu_up_noalloc(const void* x, const void* Wpacked, void* out, int64_t M, int64_t d,
+                      int64_t dff, int dtype, hipStream_t stream)
+{
+    return do_up_noalloc(x, Wpacked, out, M, d, dff, dtype, stream);
 }
 
 int mlp_forward(const void* x, const void* Wpacked, const void* Wdpacked, void* y, int64_t M,

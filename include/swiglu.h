@@ -15,9 +15,10 @@
  *   - Pointers named x, w*, out, y and workspace are DEVICE pointers on the
  *     current HIP device; the caller allocates and owns them.  The library
  *     keeps no pointer after a call returns and holds no mutable global
- *     state, so calls are thread-safe (the graph handles at the end of
- *     this header are the one exception: they keep the pointers they were
- *     captured with).
+ *     state, so calls are thread-safe (two exceptions: the graph handles at
+ *     the end of this header keep the pointers they were captured with, and
+ *     swiglu_up_noalloc works in a fixed array that its calls on one GPU
+ *     share).
  *   - dtype is SWIGLU_BF16 (bf16 storage, fp32 accumulation, bf16 output)
  *     or SWIGLU_F32 (fp32 storage and arithmetic): x, the weights and the
  *     output share that dtype.  Or SWIGLU_BF16_FP8W / SWIGLU_BF16_MXFP4W: x,
@@ -95,7 +96,8 @@ typedef enum swiglu_status {
     SWIGLU_ERR_UNSUPPORTED = -2,   /* unknown dtype, unsupported shape or path */
     SWIGLU_ERR_MISALIGNED = -3,    /* a device pointer is not 16-byte aligned */
     SWIGLU_ERR_WORKSPACE = -4,     /* workspace smaller than required */
-    SWIGLU_ERR_HIP = -5            /* a HIP launch or attribute call failed */
+    SWIGLU_ERR_HIP = -5,           /* a HIP launch or attribute call failed */
+    SWIGLU_ERR_SCRATCH = -6        /* swiglu_up_noalloc: needs more than its fixed array */
 } swiglu_status_t;
 
 /* Path selection for the *_ex entry points. */
@@ -190,6 +192,34 @@ int swiglu_up(const void *x, const void *Wpacked, void *out,
 int swiglu_up_ex(const void *x, const void *Wpacked, void *out,
                  int64_t M, int64_t d, int64_t dff, int dtype,
                  void *workspace, size_t workspace_bytes, hipStream_t stream, int path);
+
+/*
+ * swiglu_up for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc.  Same
+ * arguments, computation, dispatcher (SWIGLU_PATH_AUTO) and status codes as
+ * swiglu_up, without the workspace arguments: the workspace is a fixed
+ * array of SWIGLU_SCRATCH_BYTES (32 MiB) inside the library, one copy per
+ * GPU, held until the process ends.  It holds the split-K partial sums of
+ * the few-rows path (at most 16 MiB for any shape within the limits) and,
+ * when it fits, the packed copy of x for the many-rows path (M x d x 2
+ * bytes, rows padded to 16 and d to 64; otherwise x is read in place, with
+ * bit-identical results).  A call whose plan would need more returns
+ * SWIGLU_ERR_SCRATCH before any launch.  The call allocates nothing and
+ * calls no allocating routine; the first call on each device looks up the
+ * array's device address (hipGetSymbolAddress, no allocation), so make one
+ * call per device before capturing one into a graph.  Results are bitwise
+ * those of swiglu_up with the workspace it reports.
+ *
+ * Every call on a GPU shares that GPU's array: calls that may run at the
+ * same time on one GPU (other streams, other threads, or graph replays in
+ * flight together) race on it and must be serialised by the caller, e.g. by
+ * issuing them all on one stream.  No part of the array has to start at
+ * zero: each call writes every byte it reads.
+ */
+#define SWIGLU_SCRATCH_BYTES ((size_t)32 << 20)
+
+int swiglu_up_noalloc(const void *x, const void *Wpacked, void *out,
+                      int64_t M, int64_t d, int64_t dff, int dtype, hipStream_t stream);
 
 /*
  * y (M x d) = (silu(x . Wgate) (.) (x . Wup)) . Wdown: the MLP of the layer

@@ -38,7 +38,7 @@ def test_header_symbols_are_exported():
 
 def test_status_strings_and_version():
     assert sw.swiglu_version() == 1
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert sw.swiglu_status_string(code) != "unknown status"
     assert sw.swiglu_status_string(17) == "unknown status"
 
@@ -296,3 +296,28 @@ def test_workspace_below_the_row_major_plan_is_rejected():
         lambda: sw.mlp_block_forward(FAKE, FAKE, 1e-6, FAKE, FAKE, None, FAKE, M, d, dff, BF16,
                                      FAKE, blk_bytes, stream=0),
         sw.SWIGLU_ERR_WORKSPACE)
+
+
+def test_noalloc_rejects_bad_arguments_before_any_hip_call():
+    # the entry point without a workspace checks its arguments and its plan
+    # (which must fit the library's fixed array) before looking up the
+    # array's device address or launching anything
+    up = sw.swiglu_up_noalloc
+    assert up(FAKE, FAKE, FAKE, -1, 64, 64, BF16, stream=0) == sw.SWIGLU_ERR_INVALID_ARG
+    assert up(None, FAKE, FAKE, 4, 64, 64, BF16, stream=0) == sw.SWIGLU_ERR_INVALID_ARG
+    assert up(FAKE, FAKE, FAKE, 4, 64, 64, 7, stream=0) == sw.SWIGLU_ERR_UNSUPPORTED
+    assert up(FAKE, FAKE, FAKE, 4, 68, 64, BF16, stream=0) == sw.SWIGLU_ERR_UNSUPPORTED
+    assert up(FAKE + 4, FAKE, FAKE, 4, 64, 64, BF16, stream=0) == sw.SWIGLU_ERR_MISALIGNED
+    assert up(None, None, None, 0, 64, 64, BF16, stream=0) == sw.SWIGLU_OK
+    assert sw.swiglu_status_string(sw.SWIGLU_ERR_SCRATCH) != "unknown status"
+
+
+def test_noalloc_scratch_covers_every_plan():
+    # the array holds any shape's split-K partials (the largest, on the
+    # forced few-rows path, is 16 MiB) and the 8B-class prefill's packed x;
+    # larger packed x falls back to reading x in place
+    assert sw.swiglu_workspace_bytes_ex(256, 32768, 8, BF16, 0, sw.SWIGLU_PATH_SKINNY) <= \
+        sw.SWIGLU_SCRATCH_BYTES
+    assert sw.swiglu_workspace_bytes(4096, 4096, 14336, BF16, 0) == sw.SWIGLU_SCRATCH_BYTES
+    assert sw.swiglu_workspace_bytes(4608, 4096, 512, BF16, 0) > sw.SWIGLU_SCRATCH_BYTES
+    assert sw.swiglu_workspace_bytes_ex(4608, 4096, 512, BF16, 0, sw.SWIGLU_PATH_SKINNY) == 0
