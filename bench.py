@@ -63,6 +63,7 @@ FAMILY_SOURCES = {
     "skinny_bf16_kernel": ["skinny.hip"], "skinny_f32_kernel": ["skinny.hip"],
     "splitk_reduce_kernel": ["skinny.hip"], "wide_bf16_kernel": ["wide.hip", "wide_kernel.h"],
     "pack_act_kernel": ["pack.hip"], "rmsnorm_kernel": ["norm.hip"],
+    "mlp_fused_kernel": ["fused.hip"],
 }
 
 
@@ -298,11 +299,13 @@ class Runner:
         return a.astype(np.float64)
 
 
-PATHS = {"auto": 0, "skinny": 1, "wide": 2, "phased": 3}
-PATH_NAMES = {1: "skinny", 2: "wide", 3: "wide-phased"}
+PATHS = {"auto": 0, "skinny": 1, "wide": 2, "phased": 3, "fused": 4}
+PATH_NAMES = {1: "skinny", 2: "wide", 3: "wide-phased", 4: "fused-down"}
 
 
 def dominant_kernel(w: wl.Workload, path: int) -> str:
+    if path == 4:
+        return "mlp_fused_kernel"
     if path in (2, 3):
         return "wide_bf16_kernel"
     return "skinny_f32_kernel" if w.dtype == wl.F32 else "skinny_bf16_kernel"
@@ -492,6 +495,83 @@ def _counter_per_step(rows, order, nsteps=5):
     return out, statistics.mean(cal)
 
 
+# Extra counter passes (rocprofv3 --pmc of --probe, one directory each:
+# d/pmc_<tag>/ with its stdout in d/pmc_<tag>.log), within one pass's limits
+# (at most 8 SQ, 4 TCC, 2 GRBM counters)
+PMC_PASSES = {
+    "a": "MfmaUtil SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY "
+         "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_MFMA",
+    "b": "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_DRAM_sum SQ_LDS_BANK_CONFLICT "
+         "SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM "
+         "GRBM_GUI_ACTIVE",
+}
+
+
+def _multi_counter_per_step(rows, order, nsteps=5):
+    """Like _counter_per_step for a pass with several counters: per workload,
+    (step kernel names, [{counter: mean over the steps} per kernel])."""
+    by_disp = {}
+    for r in rows:
+        e = by_disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": {}})
+        e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [by_disp[k] for k in sorted(by_disp)]
+    names = [e["name"] for e in disp]
+    out = {}
+    for name, (a, b) in zip(order, _segments(names)):
+        step = _step_kernels(names[a:b], nsteps)
+        k = len(step)
+        per = []
+        for j in range(k):
+            runs = disp[a + j:b:k][:nsteps]
+            per.append({c: statistics.mean(x["c"][c] for x in runs) for c in runs[0]["c"]})
+        out[name] = (step, per)
+    return out
+
+
+def _counter_section(name, step, passes) -> list:
+    """Markdown lines with the extra counter passes' values for one workload."""
+    lines = []
+    for tag, data in sorted(passes.items()):
+        if name not in data:
+            continue
+        pstep, per = data[name]
+        if [kernel_family(s) for s in pstep] != [kernel_family(s) for s in step]:
+            raise ValueError("%s: pass %s launched other kernels" % (name, tag))
+        cols = sorted(per[0])
+        lines += ["", "Counters (pass %s, mean of 5 probe steps per launch): "
+                  "`cd /tmp && rocprofv3 --pmc %s --output-format csv -d <out>/pmc_%s -o probe -- "
+                  "python3 <repo>/bench.py --probe --only <workloads>`" % (tag, PMC_PASSES[tag], tag),
+                  "", "| # | kernel | " + " | ".join(cols) + " |",
+                  "|---|---|" + "---|" * len(cols)]
+        for j, s in enumerate(pstep):
+            lines.append("| %d | %s | " % (j + 1, kernel_family(s)) +
+                         " | ".join("%.4g" % per[j][c] for c in cols) + " |")
+        derived = []
+        for j, s in enumerate(pstep):
+            c = per[j]
+            parts = []
+            if "SQ_WAIT_INST_ANY" in c and c.get("SQ_WAVE_CYCLES"):
+                parts.append("waves waiting on an instruction's operands %.1f%% of their "
+                             "cycles" % (100 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]))
+            if "SQ_WAIT_ANY" in c and c.get("SQ_WAVE_CYCLES"):
+                parts.append("waiting on anything %.1f%%" %
+                             (100 * c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]))
+            if c.get("TCC_HIT_sum", 0) + c.get("TCC_MISS_sum", 0) > 0:
+                parts.append("L2 hit rate %.1f%%" % (100 * c["TCC_HIT_sum"] /
+                                                     (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])))
+            if c.get("TCC_EA0_RDREQ_sum"):
+                parts.append("%.1f%% of L2 read requests to memory marked DRAM" %
+                             (100 * c.get("TCC_EA0_RDREQ_DRAM_sum", 0) / c["TCC_EA0_RDREQ_sum"]))
+            if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+                parts.append("LDS bank-conflict cycles %.2f%% of LDS active cycles" %
+                             (100 * c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]))
+            if parts:
+                derived.append("* %s (%d): %s." % (kernel_family(s), j + 1, "; ".join(parts)))
+        if derived:
+            lines += [""] + derived
+    return lines
+
+
 def summarize(d: str) -> int:
     """Writes profiles/traffic_<workload>.json and profiles/<kernel>-<workload>.md
     from a directory of rocprofv3 runs of this script:
@@ -514,6 +594,15 @@ def summarize(d: str) -> int:
     fetch, fcal = _counter_per_step(fetch_rows, porder)
     write, wcal = _counter_per_step(write_rows, porder)
     ff, wf = (1 << 20) / fcal, (1 << 20) / wcal
+    passes = {}
+    for pdir in sorted(glob.glob(os.path.join(d, "pmc_*"))):
+        if not os.path.isdir(pdir):
+            continue
+        tag = os.path.basename(pdir)[4:]
+        plog = [ln for ln in open(pdir + ".log") if ln.startswith('{"probe_order"')]
+        passes[tag] = _multi_counter_per_step(
+            _read_csv(os.path.join(pdir, "**", "*counter_collection.csv")),
+            json.loads(plog[0])["probe_order"])
     trace_cmd = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace "
                  "-o bench -- python3 <repo>/bench.py --no-cpu")
     pmc_cmd = ("cd /tmp && rocprofv3 --pmc %s --output-format csv -d <out>/%s -o probe -- "
@@ -585,8 +674,8 @@ def summarize(d: str) -> int:
                 rl["unit"]),
             "",
             "HBM traffic per step: fetch %d B + write %d B = **%d B** against %d algorithmic "
-            "bytes (ratio %.2f)." % (sum(fb), sum(wb), total, alg, total / alg),
-            ""])
+            "bytes (ratio %.2f)." % (sum(fb), sum(wb), total, alg, total / alg)]
+            + _counter_section(name, step, passes) + [""])
         fn = os.path.join(ROOT, "profiles", "%s-%s.md" % (dom, name))
         with open(fn, "w") as f:
             f.write(md)

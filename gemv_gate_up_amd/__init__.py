@@ -38,6 +38,7 @@ SWIGLU_PATH_AUTO = 0
 SWIGLU_PATH_SKINNY = 1
 SWIGLU_PATH_WIDE = 2
 SWIGLU_PATH_WIDE_PHASED = 3
+SWIGLU_PATH_FUSED_DOWN = 4
 
 
 class SwigluError(RuntimeError):

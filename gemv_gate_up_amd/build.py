@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswiglu.so")
-SOURCES = ["api.hip", "pack.hip", "skinny.hip", "wide.hip", "norm.hip"]
+SOURCES = ["api.hip", "pack.hip", "skinny.hip", "wide.hip", "norm.hip", "fused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

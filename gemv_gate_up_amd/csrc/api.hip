@@ -54,7 +54,7 @@ int check_sizes(int64_t M, int64_t d, int64_t dff, int dtype)
 int check_path(int path)
 {
     return (path == SWIGLU_PATH_AUTO || path == SWIGLU_PATH_SKINNY || path == SWIGLU_PATH_WIDE ||
-            path == SWIGLU_PATH_WIDE_PHASED)
+            path == SWIGLU_PATH_WIDE_PHASED || path == SWIGLU_PATH_FUSED_DOWN)
                ? SWIGLU_OK
                : SWIGLU_ERR_UNSUPPORTED;
 }
@@ -93,6 +93,8 @@ GemmArgs down_args(int64_t M, int64_t d, int64_t dff, int dt)
 // product asked for it takes the one-pass kernel.
 int resolve_path(const GemmArgs& g, int path)
 {
+    if (path == SWIGLU_PATH_FUSED_DOWN)   // the MLP's fused kernel (make_plan)
+        return SWIGLU_ERR_UNSUPPORTED;
     if (path == SWIGLU_PATH_WIDE_PHASED && g.epi == EPI_PLAIN)
         path = SWIGLU_PATH_WIDE;
     if (path == SWIGLU_PATH_WIDE_PHASED)
@@ -128,9 +130,10 @@ size_t h_bytes(int64_t M, int64_t d, int64_t dff, int dt)
 // minimum size runs the same kernels on row-major activations instead.
 struct Plan {
     GemmArgs u, dn;       // the products (dn: with_down only)
-    int pu, pd;           // their paths (pd: with_down only)
+    int pu, pd;           // their paths (pd: with_down only); both FUSED_DOWN for the fused MLP
     bool packed;
     size_t h, xp, part;   // region sizes: h, packed activations, split-K partials
+    FusedPlan fu;         // the fused MLP's slices (pu == FUSED_DOWN)
     size_t need() const { return h + xp + part; }
 };
 
@@ -141,6 +144,18 @@ Plan make_plan(int64_t M, int64_t d, int64_t dff, int dt, int with_down, int pat
     Plan p;
     memset(&p, 0, sizeof p);
     p.u = up_args(M, d, dff, dt, with_down != 0);
+    if (path == SWIGLU_PATH_FUSED_DOWN) {
+        // the fused MLP: bf16 with the down projection only; its workspace
+        // holds the slices' partial y (no h, no packed activations)
+        *rc = (with_down && dt == DT_BF16) ? SWIGLU_OK : SWIGLU_ERR_UNSUPPORTED;
+        if (*rc != SWIGLU_OK)
+            return p;
+        p.dn = down_args(M, d, dff, dt);
+        p.pu = p.pd = SWIGLU_PATH_FUSED_DOWN;
+        p.fu = plan_fused(p.u, p.dn);
+        p.part = align_up(fused_partial_bytes(p.dn, p.fu));
+        return p;
+    }
     p.pu = resolve_path(p.u, path);
     *rc = p.pu < 0 ? p.pu : SWIGLU_OK;
     size_t part = p.pu < 0 ? 0 : partial_bytes(p.u, p.pu);
@@ -248,6 +263,17 @@ int do_up(const void* x, const void* wp, void* out, int64_t M, int64_t d, int64_
 int run_mlp(Plan p, const void* x, bool x_packed, const void* wp, const void* wdp, void* y,
             void* h, void* xp, void* partial, hipStream_t s, const void* resid, const void* bias)
 {
+    if (p.pu == SWIGLU_PATH_FUSED_DOWN) {
+        p.u.a = x;
+        p.u.w = wp;
+        p.dn.w = wdp;
+        p.dn.out = y;
+        p.dn.resid = resid;
+        p.dn.ldr = p.dn.ldo;
+        p.dn.bias = bias;
+        return launch_fused(p.u, p.dn, p.fu, (float*)partial, s) == hipSuccess ? SWIGLU_OK
+                                                                              : SWIGLU_ERR_HIP;
+    }
     p.u.w = wp;
     const bool h_packed = p.packed && p.pd == SWIGLU_PATH_WIDE;
     if (h_packed)

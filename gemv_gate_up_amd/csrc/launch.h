@@ -59,6 +59,24 @@ size_t skinny_partial_bytes(const GemmArgs& g, const SkinnyPlan& p);
 
 // Skinny path (skinny.hip): weights split over workgroups, fp32 accumulation.
 hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s);
+// Second pass of a split product (skinny.hip): out = epi(sum of `splits`
+// fp32 slices of partial, [slice][row][packed column], in slice order).
+hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* partial, hipStream_t s);
+
+// Fused down projection (fused.hip): y = (silu(x.Wg) * (x.Wu)) . Wd with
+// each workgroup owning a slice of d_ff: it forms its slice of h in LDS and
+// writes the slice's fp32 contribution to y; the second pass adds the
+// slices in order and applies dn's epilogue (bias, residual).  bf16 only.
+struct FusedPlan {
+    int mt;          // 16-row tiles per row group (1..4)
+    int g;           // gate/up pair blocks per d_ff slice
+    int64_t slices;  // d_ff slices = partial slices of y
+    int64_t row_groups;
+};
+FusedPlan plan_fused(const GemmArgs& up, const GemmArgs& dn);
+size_t fused_partial_bytes(const GemmArgs& dn, const FusedPlan& p);
+hipError_t launch_fused(const GemmArgs& up, const GemmArgs& dn, const FusedPlan& p, float* partial,
+                        hipStream_t s);
 
 // Wide path (wide.hip): bf16 MFMA GEMM with LDS double buffering.
 hipError_t launch_wide(const GemmArgs& g, hipStream_t s);

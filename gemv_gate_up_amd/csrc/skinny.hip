@@ -31,6 +31,8 @@
 // MXFP4 weights (WF_MXFP4) quarter them: 32 E2M1 codes per load feed four
 // MFMAs, one per 32-K chunk, and since each chunk of a column is one MX
 // block its power-of-two scale is applied by the same conversion (exact).
+#include <string.h>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -613,6 +615,25 @@ static void go_reduce(const GemmArgs& g, const SkinnyPlan& p, const float* parti
         col_blocks, (const OutT*)g.resid, g.ldr, (const OutT*)g.bias);
 }
 
+hipError_t launch_splitk_reduce(const GemmArgs& g, int splits, const float* partial, hipStream_t s)
+{
+    SkinnyPlan p;
+    memset(&p, 0, sizeof p);
+    p.splits = splits;
+    if (g.dt != DT_F32) {
+        if (g.epi == EPI_SWIGLU)
+            go_reduce<EPI_SWIGLU, uint16_t>(g, p, partial, s);
+        else
+            go_reduce<EPI_PLAIN, uint16_t>(g, p, partial, s);
+    } else {
+        if (g.epi == EPI_SWIGLU)
+            go_reduce<EPI_SWIGLU, float>(g, p, partial, s);
+        else
+            go_reduce<EPI_PLAIN, float>(g, p, partial, s);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     if (g.dt == DT_BF16) {
@@ -639,18 +660,7 @@ hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits <= 1)
         return e;
-    if (g.dt != DT_F32) {
-        if (g.epi == EPI_SWIGLU)
-            go_reduce<EPI_SWIGLU, uint16_t>(g, p, partial, s);
-        else
-            go_reduce<EPI_PLAIN, uint16_t>(g, p, partial, s);
-    } else {
-        if (g.epi == EPI_SWIGLU)
-            go_reduce<EPI_SWIGLU, float>(g, p, partial, s);
-        else
-            go_reduce<EPI_PLAIN, float>(g, p, partial, s);
-    }
-    return hipGetLastError();
+    return launch_splitk_reduce(g, p.splits, partial, s);
 }
 
 }  // namespace swg

@@ -114,7 +114,19 @@ typedef enum swiglu_path {
      * because it is slower on MI355X at every measured shape.  In
      * mlp_forward_ex it applies to the gate/up product; the down product
      * then takes SWIGLU_PATH_WIDE. */
-    SWIGLU_PATH_WIDE_PHASED = 3
+    SWIGLU_PATH_WIDE_PHASED = 3,
+    /* mlp_forward_ex / mlp_block_forward_ex only, bf16 only: the down
+     * projection fused into the gate/up kernel, the fusion of the launches
+     * that "Où part le temps d'un token" proposes in its section on what
+     * remains.  Each workgroup owns a slice of d_ff and up to 64 rows: it
+     * forms that slice of h = silu(x.Wg)*(x.Wu) in LDS (rounded to bf16, as
+     * on the other paths), multiplies it by the matching rows of Wdown and
+     * writes the slice's fp32 share of y to the workspace; a second kernel
+     * adds the slices in ascending order (deterministic, no atomics) and
+     * applies the epilogue.  h never reaches memory; the workspace holds
+     * slices x M x d fp32 values instead.  Other calls return
+     * SWIGLU_ERR_UNSUPPORTED. */
+    SWIGLU_PATH_FUSED_DOWN = 4
 } swiglu_path_t;
 
 /* Human-readable name of a status code (static string, never NULL). */

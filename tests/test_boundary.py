@@ -321,3 +321,30 @@ def test_noalloc_scratch_covers_every_plan():
     assert sw.swiglu_workspace_bytes(4096, 4096, 14336, BF16, 0) == sw.SWIGLU_SCRATCH_BYTES
     assert sw.swiglu_workspace_bytes(4608, 4096, 512, BF16, 0) > sw.SWIGLU_SCRATCH_BYTES
     assert sw.swiglu_workspace_bytes_ex(4608, 4096, 512, BF16, 0, sw.SWIGLU_PATH_SKINNY) == 0
+
+
+def test_fused_down_path_sizes_and_rejections():
+    F = sw.SWIGLU_PATH_FUSED_DOWN
+    # the fused MLP's workspace holds one fp32 slice of y (d padded to 256
+    # columns) per d_ff slice: four 16-column pair blocks per slice at 64 rows
+    slices = -(-4864 // 16) // 4
+    assert sw.swiglu_workspace_bytes_ex(64, 896, 4864, BF16, 1, F) == \
+        _al(slices * 64 * 1024 * 4)
+    # eight pair blocks per slice at up to 16 rows
+    assert sw.swiglu_workspace_bytes_ex(16, 8192, 29568, BF16, 1, F) == \
+        _al(-(-(29568 // 16) // 8) * 16 * 8192 * 4)
+    # bf16 MLPs only: swiglu_up, fp32 and quantised weights are rejected
+    # before any launch
+    assert sw.swiglu_workspace_bytes_ex(64, 896, 4864, BF16, 0, F) == 0
+    assert sw.swiglu_up_ex(FAKE, FAKE, FAKE, 4, 64, 64, BF16, None, 0, 0, F) == \
+        sw.SWIGLU_ERR_UNSUPPORTED
+    for dt in (F32, sw.SWIGLU_BF16_FP8W, sw.SWIGLU_BF16_MXFP4W):
+        assert sw.mlp_forward_ex(FAKE, FAKE, FAKE, FAKE, 4, 64, 64, dt, FAKE, 1 << 20, 0, F) == \
+            sw.SWIGLU_ERR_UNSUPPORTED
+    need = sw.swiglu_workspace_bytes_ex(64, 896, 4864, BF16, 1, F)
+    rejected_before_launch(
+        lambda: sw.mlp_forward_graph_create(FAKE, FAKE, FAKE, FAKE, 64, 896, 4864, BF16, FAKE,
+                                            need - 256, F),
+        lambda: sw.mlp_forward_ex(FAKE, FAKE, FAKE, FAKE, 64, 896, 4864, BF16, FAKE, need - 256,
+                                  0, F),
+        sw.SWIGLU_ERR_WORKSPACE)
