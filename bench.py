@@ -411,8 +411,12 @@ def measure(w: wl.Workload, inputs: Inputs, steps: int, warmup: int, copies: int
 
 
 def run_order(only):
+    """The default workloads in order, or those named (the default ones in
+    their order, then any others as given)."""
     names = CONFIGS + QUANT_CONFIGS
-    return [n for n in names if n in only] if only else names
+    if not only:
+        return names
+    return [n for n in names if n in only] + [n for n in only if n not in names]
 
 
 def probe(order) -> int:

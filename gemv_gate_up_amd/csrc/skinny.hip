@@ -533,9 +533,14 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // us, 72B 45.0 -> 44.0 us; slower at 8 rows on the 8B shape),
             // and so does a down product above 8 rows (the 72B-class MLP at
             // 16 rows 91.5 -> 84.2 us; an 8B-class gate/up product at 16
-            // rows is slower with eight: 15.7 -> 16.9 us)
+            // rows is slower with eight: 15.7 -> 16.9 us).  Above 8 rows each
+            // workgroup reads as many activation bytes as it has K, so the
+            // smaller gate/up products also take four pair blocks per wave,
+            // on eight waves (8B-class at 16 rows 15.8 -> 15.5 us)
             if (g.M > 8 && p.grid_pb >= 4 * MXFP4_WIDE_PB_CUS)
                 pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
+            else if (g.M > 8 && EPI == EPI_SWIGLU)
+                pick_split_bf16<1, 1, 4, EPI, WF, 8>(g, p, partial, s);
             else if (g.M <= 4 || (EPI == EPI_PLAIN && g.M > 8))
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else
@@ -545,11 +550,17 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // row 21.4 -> 21.0 us, two rows 21.1 -> 20.9 us; at four rows
             // 21.0 -> 21.4 us); a down product above 8 rows also on eight
             // waves, one piece per half in flight (72B-class MLP at 16 rows
-            // 130.4 -> 127.4 us)
+            // 130.4 -> 127.4 us); a gate/up product above 8 rows takes four
+            // pair blocks per wave on eight waves, one piece per half in
+            // flight: each workgroup's activation bytes (its whole K range
+            // of 16 rows) then feed twice the weights (8B-class at 16 rows
+            // 23.7 -> 23.2 us, 72B-class MLP 124.6 -> 119.8 us)
             if (g.M <= 2)
                 pick_split_bf16<1, 2, 2, EPI, WF, 8>(g, p, partial, s);
             else if (EPI == EPI_PLAIN && g.M > 8)
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
+            else if (g.M > 8)
+                pick_split_bf16<1, 1, 4, EPI, WF, 8>(g, p, partial, s);
             else
                 pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
         } else {

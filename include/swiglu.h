@@ -189,7 +189,10 @@ int swiglu_pack_down(const void *Wdown, void *Wdpacked, int64_t d, int64_t dff, 
 
 /*
  * out (M x dff) = silu(x . Wgate) (.) (x . Wup), with x M x d and Wpacked
- * from swiglu_pack_weights.  Accumulation in fp32; silu and the product in
+ * from swiglu_pack_weights: the SwiGLU product of the problem statement of
+ * "Tile-Level Activation Overlap for Efficient LLM Inference" (gate and up
+ * projections of the MLP, "Anatomie d'un transformeur sur GPU" §1.2).
+ * Accumulation in fp32; silu and the product in
  * fp32; one rounding to the output dtype at the store.  workspace (device,
  * may be NULL when swiglu_workspace_bytes returns 0) holds split-K partial
  * sums on the skinny path and the packed copy of x on the many-rows path
@@ -199,8 +202,10 @@ int swiglu_up(const void *x, const void *Wpacked, void *out,
               int64_t M, int64_t d, int64_t dff, int dtype,
               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* swiglu_up with a forced path (swiglu_path_t); WIDE or WIDE_PHASED with
- * fp32 returns SWIGLU_ERR_UNSUPPORTED. */
+/* swiglu_up (the same product, "Tile-Level Activation Overlap for Efficient
+ * LLM Inference", problem statement) with a forced path (swiglu_path_t);
+ * WIDE or WIDE_PHASED with fp32, and FUSED_DOWN, return
+ * SWIGLU_ERR_UNSUPPORTED. */
 int swiglu_up_ex(const void *x, const void *Wpacked, void *out,
                  int64_t M, int64_t d, int64_t dff, int dtype,
                  void *workspace, size_t workspace_bytes, hipStream_t stream, int path);
@@ -264,8 +269,9 @@ int mlp_forward_ex(const void *x, const void *Wpacked, const void *Wdpacked, voi
  * RMS form with a per-feature gain and a caller-given eps >= 0.
  *
  * r (M x d), gamma (d), bias (d, or NULL) and out (M x d) are device
- * arrays in the activation type of dtype (bf16 for SWIGLU_BF16 and
- * SWIGLU_BF16_FP8W, fp32 for SWIGLU_F32); Wpacked and Wdpacked as for
+ * arrays in the activation type of dtype (bf16 for SWIGLU_BF16,
+ * SWIGLU_BF16_FP8W and SWIGLU_BF16_MXFP4W, fp32 for SWIGLU_F32); Wpacked
+ * and Wdpacked as for
  * mlp_forward.  n is rounded once to the activation type; the products
  * accumulate in fp32; bias and residual are added in fp32 before the one
  * rounding of out.  out may equal r (the residual stream updated in place);

@@ -86,6 +86,12 @@ WORKLOADS = {
     "prefill8b_m4096": _wl(4, "prefill8b_m4096", 4096, 4096, 14336, BF16, False, 4096),
     "mlp72b_m16": _wl(5, "mlp72b_m16", 16, 8192, 29568, BF16, True, 2048),
     "mlp72b_m2048": _wl(5, "mlp72b_m2048", 2048, 8192, 29568, BF16, True, 2048),
+    # batches between decode and prefill (the 8B-class prefill's first rows;
+    # the 72B-class gate/up weights), on the many-rows path
+    "prefill8b_m128": _wl(4, "prefill8b_m128", 128, 4096, 14336, BF16, False, 4096),
+    "prefill8b_m256": _wl(4, "prefill8b_m256", 256, 4096, 14336, BF16, False, 4096),
+    "prefill8b_m512": _wl(4, "prefill8b_m512", 512, 4096, 14336, BF16, False, 4096),
+    "up72b_m512": _wl(5, "up72b_m512", 512, 8192, 29568, BF16, False, 2048),
     # the decode shapes with FP8 weights (same seeds, so the same bf16
     # weights before quantisation)
     "decode8b_m1_fp8w": _wl(2, "decode8b_m1_fp8w", 1, 4096, 14336, FP8W, False, 16),
