@@ -77,7 +77,20 @@ def kernel_family(name: str) -> str:
     return base.split("::")[-1].split()[-1]
 
 
-def sources_hash(kernels) -> str:
+def source_file_hashes() -> dict:
+    """sha256 of every kernel source file, as they are now."""
+    out = {}
+    d = os.path.join(ROOT, "gemv_gate_up_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            out[f] = hashlib.sha256(fh.read()).hexdigest()
+    return out
+
+
+def sources_hash(kernels, file_hashes=None) -> str:
+    """Hash of the sources the given kernels depend on: the current files,
+    or the per-file hashes a run recorded."""
+    fh = file_hashes or source_file_hashes()
     files = list(COMMON_SOURCES)
     for k in kernels:
         for f in FAMILY_SOURCES.get(kernel_family(k), []):
@@ -85,8 +98,7 @@ def sources_hash(kernels) -> str:
                 files.append(f)
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "gemv_gate_up_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        h.update(fh[f].encode())
     return h.hexdigest()[:16]
 
 
@@ -425,7 +437,7 @@ def probe(order) -> int:
     a few steps of each workload as the bench runs them (with its markers);
     prints no timing."""
     import torch
-    print(json.dumps({"probe_order": order}), flush=True)
+    print(json.dumps({"probe_order": order, "src_files": source_file_hashes()}), flush=True)
     n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda")   # no fill: a fill is a marker
     dst = torch.empty_like(src)
@@ -593,8 +605,19 @@ def summarize(d: str) -> int:
     tnames = [x["Kernel_Name"] for x in tr]
     fetch_rows = _read_csv(os.path.join(d, "fetch", "**", "*counter_collection.csv"))
     write_rows = _read_csv(os.path.join(d, "write", "**", "*counter_collection.csv"))
-    porder = json.loads([ln for ln in open(os.path.join(d, "fetch.log"))
-                         if ln.startswith('{"probe_order"')][0])["probe_order"]
+    plog = json.loads([ln for ln in open(os.path.join(d, "fetch.log"))
+                       if ln.startswith('{"probe_order"')][0])
+    porder = plog["probe_order"]
+    # every run must have been made on the same sources; the records carry
+    # the hash of those sources, not of the files as they are now
+    src = bench_line["src_files"]
+    for other in [plog] + [json.loads([ln for ln in open(os.path.join(d, f)) if
+                                       ln.startswith('{"probe_order"')][0])
+                           for f in ("write.log",) + tuple(
+                               os.path.basename(p) + ".log"
+                               for p in glob.glob(os.path.join(d, "pmc_*")) if os.path.isdir(p))]:
+        if other.get("src_files") != src:
+            raise ValueError("the runs in %s were made on different sources" % d)
     fetch, fcal = _counter_per_step(fetch_rows, porder)
     write, wcal = _counter_per_step(write_rows, porder)
     ff, wf = (1 << 20) / fcal, (1 << 20) / wcal
@@ -630,7 +653,7 @@ def summarize(d: str) -> int:
         wb = [round(v * 1024 * wf) for v in wper]
         total = sum(fb) + sum(wb)
         alg = rec["algorithmic_bytes"]
-        sha = sources_hash(step)
+        sha = sources_hash(step, src)
         traffic = {"workload": name, "src_sha": sha, "kernels": [kernel_family(s) for s in step],
                    "kernel_names": step, "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
                    "fetch_kib_raw": [round(v, 1) for v in fper],
@@ -815,6 +838,7 @@ def main() -> int:
     if quant:
         rec["quantized_decode"] = quant
     rec["order"] = executed
+    rec["src_files"] = source_file_hashes()
     print(json.dumps(rec), flush=True)
     return 0
 

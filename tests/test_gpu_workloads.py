@@ -41,7 +41,8 @@ def _rows(M):
 
 
 @pytest.mark.parametrize("name", ["tiny_decode_f32", "decode8b_m1", "decode8b_m4", "decode8b_m8",
-                                  "decode8b_m16", "prefill8b_m4096"])
+                                  "decode8b_m16", "prefill8b_m4096", "prefill8b_m128",
+                                  "prefill8b_m256", "prefill8b_m512", "up72b_m512"])
 def test_up_workload(name):
     w = wl.WORKLOADS[name]
     say("workload", name, w)
