@@ -564,7 +564,15 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             else
                 pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
         } else {
-            if (p.pb_per_wg == 2)
+            // a gate/up product above 8 rows: four pair blocks per wave, two
+            // pieces per half in flight, so each workgroup's activation
+            // bytes (its whole K range of 16 rows) feed twice the weights
+            // (8B-class at 16 rows 40.1 -> 38.3 us, 72B-class MLP at 16 rows
+            // 225.7 -> 219.0 us; eight waves, or four pieces in flight, were
+            // slower)
+            if (g.M > 8 && EPI == EPI_SWIGLU)
+                pick_split_bf16<1, 2, 4, EPI, WF>(g, p, partial, s);
+            else if (p.pb_per_wg == 2)
                 pick_split_bf16<1, 4, 2, EPI, WF>(g, p, partial, s);
             else if (g.M > 4)
                 pick_split_bf16<1, 4, 1, EPI, WF>(g, p, partial, s);
