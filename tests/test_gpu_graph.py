@@ -14,9 +14,11 @@ pytestmark = pytest.mark.gpu
 
 BF16, F32 = wl.BF16, wl.F32
 AUTO, PHASED = sw.SWIGLU_PATH_AUTO, sw.SWIGLU_PATH_WIDE_PHASED
+FUSED = sw.SWIGLU_PATH_FUSED_DOWN
 
 # (M, d, dff, dtype, with_down, path): split-K skinny with its reduce kernel,
-# the 4-launch small MLP, the wide kernels, and the fp32 skinny path
+# the 4-launch small MLP, the wide kernels, the fp32 skinny path, and the
+# fused down projection with its second pass
 CASES = [
     (1, 4096, 512, F32, False, AUTO),
     (1, 512, 2048, F32, False, AUTO),
@@ -25,6 +27,8 @@ CASES = [
     (300, 1000, 1400, BF16, False, AUTO),
     (130, 264, 712, BF16, True, AUTO),
     (257, 520, 2056, BF16, False, PHASED),
+    (64, 896, 4864, BF16, True, FUSED),
+    (20, 1032, 776, BF16, True, FUSED),
 ]
 
 
