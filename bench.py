@@ -282,14 +282,17 @@ class Runner:
         if rc != 0:
             raise RuntimeError("step failed: %s" % sw.swiglu_status_string(rc))
 
-    def time(self, steps: int, warmup: int) -> dict:
+    def time(self, steps: int, warmup: int, window=None) -> dict:
         """K back-to-back steps between two synchronisations: the host clock
         gives the step rate, and a pair of HIP events recorded on the launch
-        stream around the same K steps gives the device time per step."""
+        stream around the same K steps gives the device time per step.
+        `window` (a context manager) is entered and left around them."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
+        if window is not None:
+            window.__enter__()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -299,6 +302,8 @@ class Runner:
         e1.record(self.stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        if window is not None:
+            window.__exit__(None, None, None)
         return {"wall_ms_per_step": (t1 - t0) * 1e3 / steps,
                 "event_ms_per_step": e0.elapsed_time(e1) / steps}
 
@@ -376,12 +381,12 @@ def cpu_baseline(w: wl.Workload, inputs: Inputs, budget_s: float, nthreads: int)
 
 def measure(w: wl.Workload, inputs: Inputs, steps: int, warmup: int, copies: int,
             path: int = 0, graph: bool = False, block: bool = False,
-            check: bool = True) -> dict:
+            check: bool = True, window=None) -> dict:
     """Times one workload; returns its record (and the runner, closed)."""
     marker()
     r = Runner(w, inputs.get(w), copies, path, graph, block)
     marker()
-    t = r.time(steps, warmup)
+    t = r.time(steps, warmup, window)
     marker()
     bytes_alg = block_bytes(w) if block else w.algorithmic_bytes()
     flops_alg = w.algorithmic_flops()
@@ -420,6 +425,66 @@ def measure(w: wl.Workload, inputs: Inputs, steps: int, warmup: int, copies: int
         out["accuracy"] = accuracy(got, ref, TOL[w.dtype], what)
     r.close()
     return out
+
+
+class PowerSampler:
+    """Samples the board's socket power and graphics clocks with `amd-smi
+    metric -p -c` from a background thread while the timed steps run (after
+    the warmup); a sample counts when it falls inside [start + skip, stop]."""
+
+    CMD = ["amd-smi", "metric", "-p", "-c"]
+
+    def __init__(self, skip_s: float = 0.5, period_s: float = 0.25):
+        import threading
+        self.skip_s, self.period_s = skip_s, period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+        self.t0 = self.t1 = None
+
+    def _read(self):
+        import re
+        import subprocess
+        try:
+            txt = subprocess.run(self.CMD, capture_output=True, text=True, timeout=10).stdout
+        except (OSError, subprocess.TimeoutExpired):
+            return None
+        pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+        clks = [float(c) for c in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", txt)]
+        if not pw or not clks:
+            return None
+        return float(pw.group(1)), clks
+
+    def _loop(self):
+        while not self._stop.is_set():
+            t = time.perf_counter()
+            r = self._read()
+            if r is not None:
+                self.samples.append((t, r[0], r[1]))
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        self.t0 = time.perf_counter()
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.t1 = time.perf_counter()
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self) -> dict:
+        keep = [s for s in self.samples if self.t0 + self.skip_s <= s[0] <= self.t1]
+        out = {"command": " ".join(self.CMD), "samples": len(keep),
+               "window_s": round(self.t1 - self.t0 - self.skip_s, 2)}
+        if keep:
+            out["socket_w_mean"] = round(statistics.mean(s[1] for s in keep), 1)
+            out["socket_w_max"] = round(max(s[1] for s in keep), 1)
+            clk = [statistics.mean(s[2]) for s in keep]
+            out["gfx_mhz_mean"] = round(statistics.mean(clk), 1)
+            out["gfx_mhz_min"] = round(min(min(s[2]) for s in keep), 1)
+            out["gfx_mhz_max"] = round(max(max(s[2]) for s in keep), 1)
+        return out
 
 
 def run_order(only):
@@ -733,6 +798,10 @@ def main() -> int:
                          "workload, which needs the down projection; no configs")
     ap.add_argument("--graph", action="store_true",
                     help="replay recorded calls (HIP graphs) on the headline workload; no configs")
+    ap.add_argument("--power", action="store_true",
+                    help="sample socket power and graphics clocks (amd-smi) while the headline "
+                         "workload's timed steps run (pass --steps for a few seconds of work); "
+                         "no configs")
     ap.add_argument("--path", default="auto", choices=sorted(PATHS),
                     help="force a kernel path for the headline workload; no configs")
     ap.add_argument("--no-cpu", action="store_true")
@@ -766,7 +835,7 @@ def main() -> int:
     cores = oracle.available_cores()
     inputs = Inputs()
     hw = wl.WORKLOADS[args.workload]
-    special = args.block or args.graph or args.path != "auto"
+    special = args.block or args.graph or args.power or args.path != "auto"
 
     def steps_of(w):
         if w.name == hw.name:
@@ -779,9 +848,12 @@ def main() -> int:
         steps, warmup = steps_of(w)
         copies = weight_ring_copies(w)
         log("workload %s: %s, %d weight copies" % (w.name, w, copies))
+        sampler = PowerSampler() if args.power and headline else None
         rec = measure(w, inputs, steps, warmup, copies,
                       PATHS[args.path] if headline else 0, args.graph and headline,
-                      args.block and headline)
+                      args.block and headline, check=not sampler, window=sampler)
+        if sampler:
+            rec["power"] = sampler.summary()
         torch.cuda.empty_cache()
         if not args.no_cpu:
             budget = args.cpu_seconds if headline else args.config_cpu_seconds
@@ -827,6 +899,8 @@ def main() -> int:
     }
     if "accuracy" in head:
         rec["accuracy"] = head["accuracy"]
+    if "power" in head:
+        rec["power"] = head["power"]
     if "cpu_baseline" in head:
         rec["cpu_baseline"] = head["cpu_baseline"]
     if "prefill8b_m4096" in configs:

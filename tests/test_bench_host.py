@@ -1,0 +1,64 @@
+"""Host-side logic of bench.py that needs no GPU: the run order and the power
+sampler's parsing of `amd-smi metric -p -c` and its sample window."""
+import subprocess
+
+import bench
+
+# The shape of `amd-smi metric -p -c` on one MI355X (two of eight graphics
+# partitions shown; the values are illustrative).
+SMI_TEXT = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1393 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1889 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1968 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        MEM_0:
+            CLK: 2000 MHz
+"""
+
+
+def test_run_order_keeps_default_order_then_extras():
+    names = bench.CONFIGS + bench.QUANT_CONFIGS
+    assert bench.run_order([]) == names
+    picked = [names[3], names[1]]
+    assert bench.run_order(picked) == [names[1], names[3]]
+    assert bench.run_order(["prefill8b_m256", names[0]]) == [names[0], "prefill8b_m256"]
+
+
+def test_power_sampler_parses_socket_power_and_graphics_clocks(monkeypatch):
+    class Done:
+        stdout = SMI_TEXT
+
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: Done())
+    p = bench.PowerSampler()
+    watts, clks = p._read()
+    assert watts == 1393.0
+    assert clks == [1889.0, 1968.0]   # graphics partitions only, not the memory clock
+
+
+def test_power_sampler_unparsable_output_gives_no_sample(monkeypatch):
+    class Done:
+        stdout = "ERROR: no devices"
+
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: Done())
+    assert bench.PowerSampler()._read() is None
+
+
+def test_power_sampler_window_drops_samples_before_skip():
+    p = bench.PowerSampler(skip_s=1.0)
+    p.t0, p.t1 = 100.0, 105.0
+    p.samples = [(100.5, 900.0, [1000.0]), (101.5, 1390.0, [1900.0, 1950.0]),
+                 (104.0, 1396.0, [1880.0, 1960.0]), (105.5, 500.0, [100.0])]
+    s = p.summary()
+    assert s["samples"] == 2
+    assert s["socket_w_mean"] == 1393.0
+    assert s["socket_w_max"] == 1396.0
+    assert s["gfx_mhz_min"] == 1880.0 and s["gfx_mhz_max"] == 1960.0
+    assert s["gfx_mhz_mean"] == round((1925.0 + 1920.0) / 2, 1)
