@@ -87,6 +87,14 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
 {
     constexpr bool W8 = WF == WF_FP8;
     constexpr int CH = WF == WF_BF16 ? 1 : (WF == WF_FP8 ? 2 : 4);   // 32-K chunks per piece
+    // Software pipelining (below) for bf16 weights and one row tile, where
+    // it was measured faster: 8B-class decode at 1, 4, 8 and 16 rows
+    // 37.45, 38.3, 39.2, 38.4 -> 37.3, 37.8, 38.6, 37.6 us (with the pieces
+    // in flight re-tuned for it in pick_mt_bf16); slower with FP8 or MXFP4
+    // weights (their conversions then wait on the next step's loads: 8B
+    // decode at 16 rows 23.6 -> 25.4 us and 15.6 -> 16.2 us) and with four
+    // row tiles (0.5B-class MLP at 64 rows 19.8 -> 20.0 us).
+    constexpr bool PIPE = WF == WF_BF16 && MT == 1;
     const float* colscale = (const float*)scales;                       // FP8: per column
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -113,32 +121,36 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
             accu[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-    for (int64_t kb = kbeg + wave; kb < kend; kb += NWV * U) {
+    // One step of a wave: U pieces per half of each of its NPB pair blocks
+    // (K chunks kb, kb + NWV, ...) and the matching activation fragments.
+    struct Step {
         i32x4 wg[NPB][U], wu[NPB][U];
         uint32_t sgb[WF == WF_MXFP4 ? NPB : 1][U], sub[WF == WF_MXFP4 ? NPB : 1][U];
+        i32x4 xa[U][CH][MT];
+    };
+    auto issue = [&](int64_t kb, Step& L) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t kc = kb + NWV * u;
 #pragma unroll
             for (int p = 0; p < NPB; ++p) {
                 if (kc < kend) {
-                    wg[p][u] = load_nt16(wp + (p * nkc * 2 + kc * 2) * PIECE_VECS);
-                    wu[p][u] = load_nt16(wp + (p * nkc * 2 + kc * 2 + 1) * PIECE_VECS);
+                    L.wg[p][u] = load_nt16(wp + (p * nkc * 2 + kc * 2) * PIECE_VECS);
+                    L.wu[p][u] = load_nt16(wp + (p * nkc * 2 + kc * 2 + 1) * PIECE_VECS);
                     if constexpr (WF == WF_MXFP4) {
-                        sgb[p][u] = blkscale[(p * nkc * 2 + kc * 2) * 16];
-                        sub[p][u] = blkscale[(p * nkc * 2 + kc * 2 + 1) * 16];
+                        L.sgb[p][u] = blkscale[(p * nkc * 2 + kc * 2) * 16];
+                        L.sub[p][u] = blkscale[(p * nkc * 2 + kc * 2 + 1) * 16];
                     }
                 } else {
-                    wg[p][u] = i32x4{0, 0, 0, 0};
-                    wu[p][u] = i32x4{0, 0, 0, 0};
+                    L.wg[p][u] = i32x4{0, 0, 0, 0};
+                    L.wu[p][u] = i32x4{0, 0, 0, 0};
                     if constexpr (WF == WF_MXFP4) {
-                        sgb[p][u] = 127u * 0x01010101u;   // scale 1 for the zero padding
-                        sub[p][u] = 127u * 0x01010101u;
+                        L.sgb[p][u] = 127u * 0x01010101u;   // scale 1 for the zero padding
+                        L.sub[p][u] = 127u * 0x01010101u;
                     }
                 }
             }
         }
-        i32x4 xa[U][CH][MT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t kc = kb + NWV * u;
@@ -149,12 +161,14 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                 for (int mt = 0; mt < MT; ++mt) {
                     const int row = rbase + mt * 16 + arow;
                     if (kc < kend && row < M && k < kvalid)
-                        xa[u][ch][mt] = *(const i32x4*)(a + (int64_t)row * lda + k);
+                        L.xa[u][ch][mt] = *(const i32x4*)(a + (int64_t)row * lda + k);
                     else
-                        xa[u][ch][mt] = i32x4{0, 0, 0, 0};
+                        L.xa[u][ch][mt] = i32x4{0, 0, 0, 0};
                 }
             }
         }
+    };
+    auto consume = [&](const Step& L) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -163,20 +177,20 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                 for (int ch = 0; ch < CH; ++ch) {
                     bf16x8 bg, bu;
                     if constexpr (WF == WF_MXFP4) {
-                        bg = e2m1x8_to_bf16(wg[p][u][ch], e8m0_scale((sgb[p][u] >> (8 * ch)) & 255u));
-                        bu = e2m1x8_to_bf16(wu[p][u][ch], e8m0_scale((sub[p][u] >> (8 * ch)) & 255u));
+                        bg = e2m1x8_to_bf16(L.wg[p][u][ch], e8m0_scale((L.sgb[p][u] >> (8 * ch)) & 255u));
+                        bu = e2m1x8_to_bf16(L.wu[p][u][ch], e8m0_scale((L.sub[p][u] >> (8 * ch)) & 255u));
                     } else if constexpr (W8) {
-                        bg = ch == 0 ? e4m3x8_to_bf16(wg[p][u].x, wg[p][u].y)
-                                     : e4m3x8_to_bf16(wg[p][u].z, wg[p][u].w);
-                        bu = ch == 0 ? e4m3x8_to_bf16(wu[p][u].x, wu[p][u].y)
-                                     : e4m3x8_to_bf16(wu[p][u].z, wu[p][u].w);
+                        bg = ch == 0 ? e4m3x8_to_bf16(L.wg[p][u].x, L.wg[p][u].y)
+                                     : e4m3x8_to_bf16(L.wg[p][u].z, L.wg[p][u].w);
+                        bu = ch == 0 ? e4m3x8_to_bf16(L.wu[p][u].x, L.wu[p][u].y)
+                                     : e4m3x8_to_bf16(L.wu[p][u].z, L.wu[p][u].w);
                     } else {
-                        bg = __builtin_bit_cast(bf16x8, wg[p][u]);
-                        bu = __builtin_bit_cast(bf16x8, wu[p][u]);
+                        bg = __builtin_bit_cast(bf16x8, L.wg[p][u]);
+                        bu = __builtin_bit_cast(bf16x8, L.wu[p][u]);
                     }
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
-                        const bf16x8 av = __builtin_bit_cast(bf16x8, xa[u][ch][mt]);
+                        const bf16x8 av = __builtin_bit_cast(bf16x8, L.xa[u][ch][mt]);
                         accg[p][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bg, accg[p][mt],
                                                                                0, 0, 0);
                         accu[p][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bu, accu[p][mt],
@@ -184,6 +198,31 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
                     }
                 }
             }
+        }
+    };
+    constexpr int64_t STEP = NWV * U;
+    if constexpr (PIPE) {
+        // two register sets: a step's loads are issued before the MFMAs of
+        // the step before it, so the wave always has loads in flight
+        Step L0, L1;
+        int64_t kb = kbeg + wave;
+        if (kb < kend)
+            issue(kb, L0);
+        for (; kb < kend; kb += 2 * STEP) {
+            if (kb + STEP < kend)
+                issue(kb + STEP, L1);
+            consume(L0);
+            if (kb + STEP >= kend)
+                break;
+            if (kb + 2 * STEP < kend)
+                issue(kb + 2 * STEP, L0);
+            consume(L1);
+        }
+    } else {
+        for (int64_t kb = kbeg + wave; kb < kend; kb += STEP) {
+            Step L;
+            issue(kb, L);
+            consume(L);
         }
     }
 
@@ -564,17 +603,20 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             else
                 pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
         } else {
-            // a gate/up product above 8 rows: four pair blocks per wave, two
-            // pieces per half in flight, so each workgroup's activation
-            // bytes (its whole K range of 16 rows) feed twice the weights
-            // (8B-class at 16 rows 40.1 -> 38.3 us, 72B-class MLP at 16 rows
-            // 225.7 -> 219.0 us; eight waves, or four pieces in flight, were
-            // slower)
+            // a gate/up product above 8 rows: four pair blocks per wave, so
+            // each workgroup's activation bytes (its whole K range of 16
+            // rows) feed twice the weights (8B-class at 16 rows 40.1 -> 38.3
+            // us, 72B-class MLP at 16 rows 225.7 -> 219.0 us; eight waves, or
+            // four pieces in flight, were slower); with the pipelined loop
+            // one piece per half and step (38.4 -> 37.6 us; two: 38.4).
+            // Above two rows four pieces per half (8B-class at 4 rows 38.3
+            // -> 37.8 us pipelined; eight there: 38.8), up to two rows
+            // eight (37.3 us; four: 38.0)
             if (g.M > 8 && EPI == EPI_SWIGLU)
-                pick_split_bf16<1, 2, 4, EPI, WF>(g, p, partial, s);
+                pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
             else if (p.pb_per_wg == 2)
                 pick_split_bf16<1, 4, 2, EPI, WF>(g, p, partial, s);
-            else if (g.M > 4)
+            else if (g.M > 2)
                 pick_split_bf16<1, 4, 1, EPI, WF>(g, p, partial, s);
             else
                 pick_split_bf16<1, 8, 1, EPI, WF>(g, p, partial, s);
