@@ -474,9 +474,10 @@ static int bf16_row_tiles(int64_t M) {
     return (int)(mt > 4 ? 4 : (mt < 1 ? 1 : mt));
 }
 
-// Pair blocks per wave of the bf16 kernel: two once x's fragment is as large
-// as a weight piece (more than 8 rows), one otherwise.  FP8 weights always
-// take two (measured best at 1, 8 and 16 rows on the 8B and 72B shapes).
+// Pair blocks per wave of the bf16 kernel with bf16 weights: two once x's
+// fragment is as large as a weight piece (more than 8 rows), one otherwise.
+// For FP8 and MXFP4 weights pick_mt_bf16 sets the count by row range and
+// product (FP8 planned as two).
 static int bf16_pair_blocks(int64_t M, int dt) {
     return (dt == DT_FP8W || M > 8) ? 2 : 1;
 }
@@ -586,7 +587,10 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
         } else if constexpr (Q) {
             // FP8: up to 2 rows, eight waves per workgroup (8B decode at one
             // row 21.4 -> 21.0 us, two rows 21.1 -> 20.9 us; at four rows
-            // 21.0 -> 21.4 us); a down product above 8 rows also on eight
+            // 21.0 -> 21.4 us), each on one pair block: twice the
+            // workgroups, 3.5 per CU instead of 1.75 (one row 20.87 ->
+            // 20.68 us; four pieces per half, four waves, or two pair blocks
+            // with one piece: 21.4-22.1 us); a down product above 8 rows also on eight
             // waves, one piece per half in flight (72B-class MLP at 16 rows
             // 130.4 -> 127.4 us); a gate/up product above 8 rows takes four
             // pair blocks per wave on eight waves, one piece per half in
@@ -594,7 +598,7 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // of 16 rows) then feed twice the weights (8B-class at 16 rows
             // 23.7 -> 23.2 us, 72B-class MLP 124.6 -> 119.8 us)
             if (g.M <= 2)
-                pick_split_bf16<1, 2, 2, EPI, WF, 8>(g, p, partial, s);
+                pick_split_bf16<1, 2, 1, EPI, WF, 8>(g, p, partial, s);
             else if (EPI == EPI_PLAIN && g.M > 8)
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else if (g.M > 8)
