@@ -44,6 +44,7 @@ import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+BF16_PEAK_MHZ = 2400.0         # the graphics clock that peak assumes
 METRIC = "fused SwiGLU MLP: HBM GB/s at M=1 decode; bf16 TFLOP/s at M=4096 prefill"
 HEADLINE = "decode8b_m1"
 # the workload configurations, in run order
@@ -381,13 +382,14 @@ def cpu_baseline(w: wl.Workload, inputs: Inputs, budget_s: float, nthreads: int)
 
 def measure(w: wl.Workload, inputs: Inputs, steps: int, warmup: int, copies: int,
             path: int = 0, graph: bool = False, block: bool = False,
-            check: bool = True, window=None) -> dict:
+            check: bool = True, window=None, markers: bool = True) -> dict:
     """Times one workload; returns its record (and the runner, closed)."""
-    marker()
+    mark = marker if markers else (lambda: None)
+    mark()
     r = Runner(w, inputs.get(w), copies, path, graph, block)
-    marker()
+    mark()
     t = r.time(steps, warmup, window)
-    marker()
+    mark()
     bytes_alg = block_bytes(w) if block else w.algorithmic_bytes()
     flops_alg = w.algorithmic_flops()
     ms = t["event_ms_per_step"]
@@ -485,6 +487,29 @@ class PowerSampler:
             out["gfx_mhz_min"] = round(min(min(s[2]) for s in keep), 1)
             out["gfx_mhz_max"] = round(max(max(s[2]) for s in keep), 1)
         return out
+
+
+# The matrix-bound workload whose board power and clock the default run
+# records: under it the board sits at its power limit and the clock drops.
+POWER_WORKLOAD = "prefill8b_m4096"
+
+
+def power_window(w: wl.Workload, inputs: Inputs, rec: dict, seconds: float, copies: int) -> dict:
+    """Runs the workload again for about `seconds` of timed steps (untimed
+    for the record) while sampling board power and clocks; adds the
+    fraction of the bf16 peak at the mean sampled clock."""
+    ms = rec["roofline"]["event_ms_per_step"]
+    steps = max(20, int(seconds * 1e3 / ms))
+    sampler = PowerSampler(skip_s=1.0)   # the board's power control settles within about a second
+    # no markers: a trace's per-workload segments stay as the timed run cut them
+    measure(w, inputs, steps, 20, copies, check=False, window=sampler, markers=False)
+    out = sampler.summary()
+    out["steps"] = steps
+    if out.get("gfx_mhz_mean"):
+        at_clock = BF16_PEAK_TFLOPS * out["gfx_mhz_mean"] / BF16_PEAK_MHZ
+        out["peak_at_clock_tflops"] = round(at_clock, 1)
+        out["frac_at_clock"] = round(rec["roofline"]["achieved"] / at_clock, 4)
+    return out
 
 
 def run_order(only):
@@ -696,7 +721,7 @@ def summarize(d: str) -> int:
             _read_csv(os.path.join(pdir, "**", "*counter_collection.csv")),
             json.loads(plog[0])["probe_order"])
     trace_cmd = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace "
-                 "-o bench -- python3 <repo>/bench.py --no-cpu")
+                 "-o bench -- python3 <repo>/bench.py --no-cpu --power-seconds 0")
     pmc_cmd = ("cd /tmp && rocprofv3 --pmc %s --output-format csv -d <out>/%s -o probe -- "
                "python3 <repo>/bench.py --probe")
     for name, (a, b) in zip(order, _segments(tnames)):
@@ -802,6 +827,9 @@ def main() -> int:
                     help="sample socket power and graphics clocks (amd-smi) while the headline "
                          "workload's timed steps run (pass --steps for a few seconds of work); "
                          "no configs")
+    ap.add_argument("--power-seconds", type=float, default=4.0,
+                    help="seconds of extra %s steps under the power sampler in the default "
+                         "run (0: none)" % POWER_WORKLOAD)
     ap.add_argument("--path", default="auto", choices=sorted(PATHS),
                     help="force a kernel path for the headline workload; no configs")
     ap.add_argument("--no-cpu", action="store_true")
@@ -854,6 +882,8 @@ def main() -> int:
                       args.block and headline, check=not sampler, window=sampler)
         if sampler:
             rec["power"] = sampler.summary()
+        elif w.name == POWER_WORKLOAD and not special and args.power_seconds > 0:
+            rec["power"] = power_window(w, inputs, rec, args.power_seconds, copies)
         torch.cuda.empty_cache()
         if not args.no_cpu:
             budget = args.cpu_seconds if headline else args.config_cpu_seconds
@@ -906,7 +936,8 @@ def main() -> int:
     if "prefill8b_m4096" in configs:
         p = configs["prefill8b_m4096"]
         rec["prefill"] = {k: p[k] for k in ("workload", "M", "d", "dff", "value", "unit",
-                                            "ms_per_step", "steps", "warmup", "roofline")}
+                                            "ms_per_step", "steps", "warmup", "roofline",
+                                            "power") if k in p}
     if configs:
         rec["configs"] = configs
     if quant:

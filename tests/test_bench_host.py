@@ -62,3 +62,30 @@ def test_power_sampler_window_drops_samples_before_skip():
     assert s["socket_w_max"] == 1396.0
     assert s["gfx_mhz_min"] == 1880.0 and s["gfx_mhz_max"] == 1960.0
     assert s["gfx_mhz_mean"] == round((1925.0 + 1920.0) / 2, 1)
+
+
+def test_power_window_fraction_at_the_sampled_clock(monkeypatch):
+    # the extra steps run through measure(); here they only feed the sampler
+    class FakeSampler:
+        def __init__(self, skip_s=0.5):
+            self.skip_s = skip_s
+
+        def summary(self):
+            return {"samples": 3, "gfx_mhz_mean": 1800.0}
+
+    monkeypatch.setattr(bench, "PowerSampler", FakeSampler)
+    seen = {}
+
+    def fake_measure(w, inputs, steps, warmup, copies, check=True, window=None, markers=True):
+        seen.update(steps=steps, check=check, window=window, markers=markers)
+        return {}
+
+    monkeypatch.setattr(bench, "measure", fake_measure)
+    rec = {"roofline": {"event_ms_per_step": 0.5, "achieved": 1320.0}}
+    out = bench.power_window(bench.wl.WORKLOADS["prefill8b_m4096"], None, rec, 2.5, 1)
+    assert seen["steps"] == 5000 and seen["check"] is False and seen["markers"] is False
+    assert isinstance(seen["window"], FakeSampler) and seen["window"].skip_s == 1.0
+    at_clock = bench.BF16_PEAK_TFLOPS * 1800.0 / 2400.0
+    assert out["peak_at_clock_tflops"] == round(at_clock, 1)
+    assert out["frac_at_clock"] == round(1320.0 / at_clock, 4)
+    assert out["steps"] == 5000
