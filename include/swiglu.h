@@ -229,9 +229,12 @@ int swiglu_up_ex(const void *x, const void *Wpacked, void *out,
  *
  * Every call on a GPU shares that GPU's array: calls that may run at the
  * same time on one GPU (other streams, other threads, or graph replays in
- * flight together) race on it and must be serialised by the caller, e.g. by
- * issuing them all on one stream.  No part of the array has to start at
- * zero: each call writes every byte it reads.
+ * flight together) race on it and must be serialised by the caller: issue
+ * them on one stream and, when several host threads make them, one call at
+ * a time (a call enqueues up to two kernels, the split product and its
+ * second pass, which another call's kernels must not come between).  No
+ * part of the array has to start at zero: each call writes every byte it
+ * reads.
  */
 #define SWIGLU_SCRATCH_BYTES ((size_t)32 << 20)
 
