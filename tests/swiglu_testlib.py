@@ -1,7 +1,7 @@
 """Helpers shared by the GPU tests: move seeded inputs to the device, call
 the library through its C ABI, bring results back as fp64, and compare
-them with the oracle under the benchmark spec's tolerance rule
-|gpu - ref| <= tol * (1 + |ref|)."""
+them with the oracle under the tolerance rule
+|gpu - ref| <= tol * (1 + |ref|) (tol 2e-2 for bf16 outputs, 1e-4 for fp32)."""
 from __future__ import annotations
 
 import sys
