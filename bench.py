@@ -335,18 +335,114 @@ def block_bytes(w: wl.Workload) -> int:
     return w.algorithmic_bytes() + 2 * w.d * w.elem_bytes
 
 
-def accuracy(got: np.ndarray, ref: np.ndarray, tol: float, what: str) -> dict:
+def max_ulps(err: np.ndarray, ref: np.ndarray, mant_bits: int) -> float:
+    """Largest error in units in the last place of the reference, at an output
+    precision of `mant_bits` explicit mantissa bits (7 for bf16, 23 for fp32);
+    references below the smallest normal fp32 are left out."""
+    a = np.abs(ref)
+    normal = a >= 2.0 ** -126
+    if not normal.any():
+        return 0.0
+    ulp = np.exp2(np.floor(np.log2(a[normal])) - mant_bits)
+    return float((err[normal] / ulp).max())
+
+
+def accuracy(got: np.ndarray, ref: np.ndarray, tol: float, what: str, dot_scale=None,
+             mant_bits: int = 7) -> dict:
     """Pass/fail under |gpu - ref| <= tol (1 + |ref|), with the diagnostics:
-    max error, max scaled error, and the share of elements off by more than
-    1% of |ref| (elements with |ref| > 1e-3)."""
+    max error, max scaled error, the share of elements off by more than 1% of
+    |ref| (elements with |ref| > 1e-3), the largest error in ulps of the
+    reference, and (given dot_scale, the |a|.|b| scale of each output's sums)
+    the largest error against that scale."""
     err = np.abs(got - ref)
     scaled = err / (1.0 + np.abs(ref))
     big = np.abs(ref) > 1e-3
     rel = np.where(big, err / np.maximum(np.abs(ref), 1e-300), 0.0)
-    return {"checked": what, "elements": int(got.size), "tol": tol,
-            "ok": bool(np.all(np.isfinite(got)) and np.all(scaled <= tol)),
-            "max_abs": float(err.max()), "max_scaled": float(scaled.max()),
-            "frac_rel_gt_1pct": float((rel > 0.01).sum() / max(1, big.sum()))}
+    out = {"checked": what, "elements": int(got.size), "tol": tol,
+           "ok": bool(np.all(np.isfinite(got)) and np.all(scaled <= tol)),
+           "max_abs": float(err.max()), "max_scaled": float(scaled.max()),
+           "frac_rel_gt_1pct": float((rel > 0.01).sum() / max(1, big.sum())),
+           "max_ulps": max_ulps(err, ref, mant_bits)}
+    if dot_scale is not None:
+        pos = dot_scale > 0
+        out["max_err_over_dot_scale"] = float((err[pos] / dot_scale[pos]).max()) if pos.any() else 0.0
+    return out
+
+
+def _abs_storage(a: np.ndarray) -> np.ndarray:
+    """|a| in the same storage: bf16 bit patterns lose their sign bit."""
+    if a.dtype == np.uint16:
+        return a & np.uint16(0x7FFF)
+    return np.abs(a)
+
+
+_E4M3_TABLE = []
+
+
+def _e4m3_table() -> np.ndarray:
+    """The 256 E4M3 code values (the oracle's decoder), built once."""
+    if not _E4M3_TABLE:
+        import oracle
+        _E4M3_TABLE.append(np.array([oracle.e4m3_to_double(c) for c in range(256)],
+                                    dtype=np.float32))
+    return _E4M3_TABLE[0]
+
+
+def _as_f32(a) -> np.ndarray:
+    """A matrix's values as float32: bf16 bit patterns widened (exact), fp32
+    or fp64 arrays, or E4M3 (codes, per-column scales) pairs decoded."""
+    if isinstance(a, tuple):
+        codes, scales = a
+        return _e4m3_table()[codes] * scales[None, :]
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32)
+    return a.astype(np.float32, copy=False)
+
+
+def _row_products(xr: np.ndarray, W, absolute: bool):
+    """xr . W and, with `absolute`, |xr| . |W| (fp64 results), decoding W to
+    float32 2048 of its rows at a time so no full-size copy is made."""
+    K = W[0].shape[0] if isinstance(W, tuple) else np.asarray(W).shape[0]
+    n = W[0].shape[1] if isinstance(W, tuple) else np.asarray(W).shape[1]
+    out = np.zeros((xr.shape[0], n))
+    aout = np.zeros((xr.shape[0], n)) if absolute else None
+    for k0 in range(0, K, 2048):
+        k1 = min(K, k0 + 2048)
+        blk = _as_f32((W[0][k0:k1], W[1]) if isinstance(W, tuple) else np.asarray(W)[k0:k1])
+        xs = xr[:, k0:k1].astype(np.float32)
+        out += xs @ blk
+        if absolute:
+            aout += np.abs(xs) @ np.abs(blk)
+    return out, aout
+
+
+def dot_scale(w: wl.Workload, x: np.ndarray, wts: dict, rows) -> np.ndarray:
+    """The error scale of each output's sums, the |a|.|b| rule of "Où part le
+    temps d'un token" (section on the narrow-matrix kernel) carried through
+    the step, for the given rows of x: for out = silu(g) u,
+    |d out/d g| sum|x||wg| + |d out/d u| sum|x||wu|; for y = out . Wd, the
+    sum over d_ff of |out||wd|.  A diagnostic of the size of the rounding a
+    correct fp32-accumulated result can show, computed in float32 from the
+    weights as stored (quantised weights decoded), not a reference value."""
+    xa = np.asarray(x)
+    xr = _as_f32(xa if rows is None else xa[list(rows)]).astype(np.float64)
+    down = w.with_down
+    g, sg = _row_products(xr, wts["wg"], not down)
+    u, su = _row_products(xr, wts["wu"], not down)
+    sig = np.where(g >= 0, 1.0 / (1.0 + np.exp(-np.abs(g))),
+                   np.exp(-np.abs(g)) / (1.0 + np.exp(-np.abs(g))))
+    if down:
+        _, sy = _row_products(np.abs(g * sig * u), wts["wd"], True)
+        return sy
+    return np.abs(u * sig * (1.0 + g * (1.0 - sig))) * sg + np.abs(g * sig) * su
+
+
+def scale_rows(rows, M: int):
+    """The rows the |a|.|b| diagnostic covers: the first and last of those
+    checked (at most two, to keep the 72B-class weights' extra passes short)."""
+    r = list(range(M)) if rows is None else list(rows)
+    return sorted({r[0], r[-1]})
 
 
 def cpu_baseline(w: wl.Workload, inputs: Inputs, budget_s: float, nthreads: int) -> dict:
@@ -421,10 +517,24 @@ def measure(w: wl.Workload, inputs: Inputs, steps: int, warmup: int, copies: int
         rows = sample_rows(w.M)
         got = r.result(rows)
         inp = inputs.get(w)
-        ref = oracle_call(w, inp["x"][:w.M], inputs.weights_for_oracle(w), rows=rows)
+        wts = inputs.weights_for_oracle(w)
+        ref = oracle_call(w, inp["x"][:w.M], wts, rows=rows)
         what = ("every output" if rows is None else
                 "%d whole rows (one per 256-row tile and the last)" % len(rows))
-        out["accuracy"] = accuracy(got, ref, TOL[w.dtype], what)
+        acc = accuracy(got, ref, TOL[w.dtype], what, None, 23 if w.dtype == wl.F32 else 7)
+        srows = scale_rows(rows, w.M)
+        pos = [i for i, r in enumerate(list(range(w.M)) if rows is None else list(rows))
+               if r in srows]
+        sc = dot_scale(w, inp["x"][:w.M], wts, srows)
+        err = np.abs(got[pos] - ref[pos])
+        ok = sc > 0
+        acc["max_err_over_dot_scale"] = float((err[ok] / sc[ok]).max()) if ok.any() else 0.0
+        # ulps where the sum did not cancel to well below its terms' scale
+        cond = np.abs(ref[pos]) >= 0.01 * sc
+        acc["max_ulps_well_conditioned"] = max_ulps(err[cond], ref[pos][cond],
+                                                    23 if w.dtype == wl.F32 else 7)
+        acc["dot_scale_rows"] = srows
+        out["accuracy"] = acc
     r.close()
     return out
 

@@ -89,3 +89,63 @@ def test_power_window_fraction_at_the_sampled_clock(monkeypatch):
     assert out["peak_at_clock_tflops"] == round(at_clock, 1)
     assert out["frac_at_clock"] == round(1320.0 / at_clock, 4)
     assert out["steps"] == 5000
+
+
+def test_max_ulps_at_bf16_and_fp32_precision():
+    import numpy as np
+    ref = np.array([1.0, -3.0, 0.0])
+    err = np.array([2.0 ** -8, 2.0 ** -7, 5.0])   # 0.5 ulp of 1 (2^-7), 0.5 ulp of 3 (2^-6); zero skipped
+    assert bench.max_ulps(err, ref, 7) == 0.5
+    assert bench.max_ulps(np.array([2.0 ** -23]), np.array([1.0]), 23) == 1.0
+    assert bench.max_ulps(np.array([1.0]), np.array([0.0]), 7) == 0.0
+
+
+def _decoded(inp):
+    import oracle
+    return {k: oracle.to_double(v) for k, v in inp.items()}
+
+
+def test_dot_scale_of_swiglu_outputs():
+    # against numpy on the decoded values: |d h/d g| sum|x||wg| + |d h/d u| sum|x||wu|
+    import numpy as np
+    w = bench.wl.Workload(0, "t", 3, 16, 24, bench.wl.BF16, False, 3)
+    inp = bench.wl.random_inputs(77, 3, 16, 24, bench.wl.BF16)
+    got = bench.dot_scale(w, inp["x"], {"wg": inp["wg"], "wu": inp["wu"]}, None)
+    f = _decoded(inp)
+    g, u = f["x"] @ f["wg"], f["x"] @ f["wu"]
+    sg, su = np.abs(f["x"]) @ np.abs(f["wg"]), np.abs(f["x"]) @ np.abs(f["wu"])
+    sig = 1.0 / (1.0 + np.exp(-g))
+    want = np.abs(u * sig * (1 + g * (1 - sig))) * sg + np.abs(g * sig) * su
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=0)   # float32 arithmetic
+
+
+def test_dot_scale_of_mlp_outputs():
+    import numpy as np
+    import oracle
+    w = bench.wl.Workload(0, "t", 2, 16, 24, bench.wl.BF16, True, 2)
+    inp = bench.wl.random_inputs(78, 2, 16, 24, bench.wl.BF16, with_down=True)
+    wts = {k: inp[k] for k in ("wg", "wu", "wd")}
+    got = bench.dot_scale(w, inp["x"], wts, [1])
+    f = _decoded(inp)
+    h = oracle.swiglu(inp["x"], inp["wg"], inp["wu"])
+    want = np.abs(h[1:2]) @ np.abs(f["wd"])
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=0)
+
+
+def test_accuracy_record_reports_the_new_diagnostics():
+    import numpy as np
+    ref = np.array([[1.0, 2.0]])
+    got = ref + np.array([[2.0 ** -9, 0.0]])
+    rec = bench.accuracy(got, ref, 2e-2, "test", np.array([[0.5, 0.0]]), 7)
+    assert rec["ok"] and rec["max_ulps"] == 0.25
+    assert rec["max_err_over_dot_scale"] == 2.0 ** -9 / 0.5
+
+
+def test_as_f32_decodes_each_storage():
+    import numpy as np
+    import oracle
+    w = bench.wl.to_storage(bench.wl.normal(5, (8, 16), 0.5), bench.wl.BF16)
+    np.testing.assert_array_equal(bench._as_f32(w).astype(np.float64), oracle.to_double(w))
+    codes, scales = oracle.quantize_e4m3(w)
+    np.testing.assert_allclose(bench._as_f32((codes, scales)),
+                               oracle.dequantize_e4m3(codes, scales), rtol=1e-7, atol=0)
