@@ -478,7 +478,8 @@ def cpu_baseline(w: wl.Workload, inputs: Inputs, budget_s: float, nthreads: int)
 
 def measure(w: wl.Workload, inputs: Inputs, steps: int, warmup: int, copies: int,
             path: int = 0, graph: bool = False, block: bool = False,
-            check: bool = True, window=None, markers: bool = True) -> dict:
+            check: bool = True, window=None, markers: bool = True,
+            read_ceilings: bool = True) -> dict:
     """Times one workload; returns its record (and the runner, closed)."""
     mark = marker if markers else (lambda: None)
     mark()
@@ -506,6 +507,10 @@ def measure(w: wl.Workload, inputs: Inputs, steps: int, warmup: int, copies: int
     roof["kernel"] = kern
     roof["step_kernels"] = rec["kernels"] if rec else None
     roof["event_ms_per_step"] = round(ms, 5)
+    if hbm_bound(w) and read_ceilings:
+        rc = read_ceiling(bytes_alg)
+        roof["read_ceiling"] = rc
+        roof["frac_of_read_ceiling"] = round(achieved / rc["gbps"], 4)
     out = {"workload": w.name, "M": w.M, "d": w.d, "dff": w.dff,
            "dtype": wl.DTYPE_NAMES[w.dtype], "with_down": w.with_down,
            "path": PATH_NAMES[r.path], "weight_copies": copies, "steps": steps, "warmup": warmup,
@@ -612,7 +617,8 @@ def power_window(w: wl.Workload, inputs: Inputs, rec: dict, seconds: float, copi
     steps = max(20, int(seconds * 1e3 / ms))
     sampler = PowerSampler(skip_s=1.0)   # the board's power control settles within about a second
     # no markers: a trace's per-workload segments stay as the timed run cut them
-    measure(w, inputs, steps, 20, copies, check=False, window=sampler, markers=False)
+    measure(w, inputs, steps, 20, copies, check=False, window=sampler, markers=False,
+            read_ceilings=False)
     out = sampler.summary()
     out["steps"] = steps
     if out.get("gfx_mhz_mean"):
@@ -620,6 +626,82 @@ def power_window(w: wl.Workload, inputs: Inputs, rec: dict, seconds: float, copi
         out["peak_at_clock_tflops"] = round(at_clock, 1)
         out["frac_at_clock"] = round(rec["roofline"]["achieved"] / at_clock, 4)
     return out
+
+
+_PROBE = []
+_READ_CEILINGS = {}
+
+
+def _probe_lib():
+    """The measurement-aid library built beside libswiglu.so (a plain read,
+    device attributes); loaded once."""
+    if not _PROBE:
+        import ctypes
+        lib = ctypes.CDLL(os.path.join(ROOT, "gemv_gate_up_amd", "libswiglu_probe.so"))
+        lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.probe_device.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+        _PROBE.append(lib)
+    return _PROBE[0]
+
+
+def read_ceiling(nbytes: int) -> dict:
+    """The best time of a plain streaming read of nbytes (the probe library's
+    grid-stride kernel: 512-4096 workgroups, 4-16 nontemporal 16-byte loads
+    in flight per thread) over a ring of copies of at least 1 GiB, so that
+    the Infinity Cache serves none of it: the HBM rate a kernel can reach at
+    this size on this board.  Cached per size."""
+    nb = int(nbytes) // 16 * 16
+    if nb in _READ_CEILINGS:
+        return _READ_CEILINGS[nb]
+    import torch
+    lib = _probe_lib()
+    copies = max(2, -(-(1 << 30) // nb))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    stream = torch.cuda.current_stream()
+    best = None
+    for grid in (512, 1024, 2048, 4096):
+        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+        for u in (4, 8, 16):
+            def go(i):
+                rc = lib.probe_read(bufs[i % copies].data_ptr(), nb, sink.data_ptr(), grid, u,
+                                    stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError("probe_read failed (%d)" % rc)
+            for i in range(10):
+                go(i)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            n = 30
+            e0.record(stream)
+            for i in range(n):
+                go(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / n * 1e3
+            if best is None or us < best[0]:
+                best = (us, grid, u)
+    del bufs
+    torch.cuda.empty_cache()
+    rec = {"bytes": nb, "us": round(best[0], 3), "gbps": round(nb / best[0] / 1e3, 1),
+           "grid": best[1], "loads_in_flight": best[2]}
+    _READ_CEILINGS[nb] = rec
+    return rec
+
+
+def device_record() -> dict:
+    """The device's compute units and maximum graphics clock (HIP device
+    attributes) and the dense bf16 matrix peak they give: 4096 FLOPs per
+    clock per CU."""
+    import ctypes
+    import torch
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    rc = _probe_lib().probe_device(ctypes.byref(cus), ctypes.byref(khz))
+    if rc != 0:
+        return {"error": rc}
+    return {"name": torch.cuda.get_device_name(0), "compute_units": cus.value,
+            "max_clock_mhz": khz.value / 1000.0,
+            "bf16_peak_tflops": round(cus.value * 4096 * khz.value * 1e3 / 1e12, 1)}
 
 
 def run_order(only):
@@ -1052,6 +1134,7 @@ def main() -> int:
         rec["configs"] = configs
     if quant:
         rec["quantized_decode"] = quant
+    rec["device"] = device_record()
     rec["order"] = executed
     rec["src_files"] = source_file_hashes()
     print(json.dumps(rec), flush=True)

@@ -1,4 +1,5 @@
-"""Builds libswiglu.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Builds libswiglu.so (the C-ABI library) in-tree with hipcc for gfx950, and
+libswiglu_probe.so, bench.py's measurement aids.
 
 Usage: python gemv_gate_up_amd/build.py   (or build() from Python; this file
 is loaded by path so that it never imports the package, whose import needs
@@ -18,6 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswiglu.so")
 SOURCES = ["api.hip", "pack.hip", "skinny.hip", "wide.hip", "norm.hip", "fused.hip"]
+# measurement aids for bench.py (a plain streaming read, device attributes),
+# kept out of the library: their own shared object
+PROBE_SRC = os.path.join(PKG, "probe", "read_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libswiglu_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -47,8 +52,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + CFLAGS + ["-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the probe library:\n" + r.stderr)
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

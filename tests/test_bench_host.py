@@ -76,14 +76,17 @@ def test_power_window_fraction_at_the_sampled_clock(monkeypatch):
     monkeypatch.setattr(bench, "PowerSampler", FakeSampler)
     seen = {}
 
-    def fake_measure(w, inputs, steps, warmup, copies, check=True, window=None, markers=True):
-        seen.update(steps=steps, check=check, window=window, markers=markers)
+    def fake_measure(w, inputs, steps, warmup, copies, check=True, window=None, markers=True,
+                     read_ceilings=True):
+        seen.update(steps=steps, check=check, window=window, markers=markers,
+                    read_ceilings=read_ceilings)
         return {}
 
     monkeypatch.setattr(bench, "measure", fake_measure)
     rec = {"roofline": {"event_ms_per_step": 0.5, "achieved": 1320.0}}
     out = bench.power_window(bench.wl.WORKLOADS["prefill8b_m4096"], None, rec, 2.5, 1)
     assert seen["steps"] == 5000 and seen["check"] is False and seen["markers"] is False
+    assert seen["read_ceilings"] is False
     assert isinstance(seen["window"], FakeSampler) and seen["window"].skip_s == 1.0
     at_clock = bench.BF16_PEAK_TFLOPS * 1800.0 / 2400.0
     assert out["peak_at_clock_tflops"] == round(at_clock, 1)
