@@ -130,7 +130,9 @@ pack_fp8_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ 
 // MXFP4: one thread per (pair block, k piece, half, column, chunk), in the
 // order of the scale table, so thread t writes byte t: the E8M0 code of the
 // block's shared exponent floor(log2 amax) - 2, clamped to [-126, 127]
-// (code 127, exponent 0, for an all-zero block).
+// (code 127, exponent 0, for an all-zero block).  A NaN weight does not
+// count toward amax (fmaxf drops it); an infinite amax takes the clamp's
+// top, 127.
 __global__ void __launch_bounds__(256)
 mx_scale_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ src1,
                 uint8_t* __restrict__ scales, int64_t K, int64_t N, int64_t nkc, int64_t total,
@@ -149,7 +151,9 @@ mx_scale_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ 
         for (int64_t k = k0; k < k0 + 32 && k < K; ++k)
             amax = fmaxf(amax, fabsf(bf16_to_f32(src[k * N + n])));
     int s = 0;
-    if (amax > 0.f) {
+    if (amax == __builtin_inff()) {
+        s = 127;
+    } else if (amax > 0.f) {
         int e;
         frexpf(amax, &e);             // amax = f * 2^e, f in [0.5, 1)
         s = e - 1 - 2;
@@ -160,7 +164,8 @@ mx_scale_kernel(const uint16_t* __restrict__ src0, const uint16_t* __restrict__ 
 
 // E2M1 code of q: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the
 // even code (the thresholds below are the midpoints; a tie lands on the
-// side whose code is even), saturating at 6; the sign goes to bit 3.
+// side whose code is even), saturating at 6; the sign goes to bit 3.  E2M1
+// has no infinity or NaN: both fall through every comparison to code 7.
 __device__ __forceinline__ uint32_t e2m1_code(float q) {
     const uint32_t sign = (__builtin_bit_cast(uint32_t, q) >> 28) & 8u;
     const float a = fabsf(q);

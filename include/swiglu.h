@@ -66,7 +66,10 @@ typedef enum swiglu_dtype {
      * magnitude in the column) / 448 in fp32, codes = OCP E4M3 (no
      * infinities; largest value 448) nearest to w / scale (an fp32
      * division), ties to the even code, saturating; an all-zero column
-     * gets scale 0.  The kernels widen the codes exactly to bf16, multiply
+     * gets scale 0.  A NaN weight does not count toward the scale and takes
+     * E4M3's NaN code 0x7F (code 0 if the column's scale is 0, like every
+     * code of such a column); an infinite one makes the scale infinite.
+     * The kernels widen the codes exactly to bf16, multiply
      * on the matrix unit with fp32 accumulation and apply the column scale
      * to the finished sum.  Served by the skinny path only (any M; it is
      * built for M <= 64): SWIGLU_PATH_WIDE and WIDE_PHASED return
@@ -81,7 +84,11 @@ typedef enum swiglu_dtype {
      * block's shared exponent is floor(log2(largest magnitude)) - 2,
      * clamped to [-126, 127] (0 for an all-zero block), and each code is
      * the E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6) nearest to w / 2^s, ties
-     * to the even code, saturating at 6.  The kernels widen codes and scale
+     * to the even code, saturating at 6.  E2M1 has no infinity or NaN: such
+     * weights are coded +-6 with their sign bit, a NaN does not count toward
+     * the largest magnitude and an infinite one sets s = 127 (the block
+     * becomes useless, but nothing is undefined; the MX block-NaN scale is
+     * not used).  The kernels widen codes and scale
      * exactly to bf16 (gfx950's scaled FP4 conversion), multiply on the
      * matrix unit with fp32 accumulation.  Skinny path only, like
      * SWIGLU_BF16_FP8W; K is padded to 128 and the packed buffers hold half

@@ -162,6 +162,13 @@ int oracle_quantize_e4m3_columns(const uint16_t *w, int64_t K, int64_t N, uint8_
  * exact; the element code is the nearest E2M1 value, ties to the even code,
  * saturating at +-6.
  *
+ * Non-finite weights (the format defines no code for them; this is the
+ * reading taken here): E2M1 has neither infinity nor NaN, so both saturate
+ * to +-6 with their sign bit; a NaN does not count toward amax (it compares
+ * false), and an infinite amax takes the clamp's top, s = 127, since
+ * floor(log2(inf)) is infinite.  The MX block-NaN scale code 0xFF is not
+ * used: a NaN weight does not make its block NaN.
+ *
  * E2M1: sign bit 3, exponent bits 2-1 with bias 1, mantissa bit 0; exponent
  * 0 holds the subnormal 0.5 * m, otherwise (1 + m/2) * 2^(e-1): the values
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6.
@@ -179,7 +186,7 @@ uint8_t oracle_e2m1_from_double(double v)
 {
     uint8_t sign = signbit(v) ? 0x8 : 0x0;
     double a = fabs(v);
-    if (a >= 6.0)
+    if (!(a < 6.0))                 /* 6 and beyond, infinities, NaN */
         return sign | 0x7;
     int e;
     frexp(a, &e);
@@ -197,8 +204,10 @@ uint8_t oracle_e2m1_from_double(double v)
 /* Shared exponent of a block with largest magnitude amax (see above). */
 int oracle_mx_shared_exponent(double amax)
 {
-    if (amax == 0.0)
+    if (amax == 0.0 || isnan(amax))
         return 0;
+    if (isinf(amax))
+        return 127;
     int e;
     frexp(amax, &e);
     int s = (e - 1) - 2;

@@ -50,6 +50,13 @@ def test_pack_matches_the_oracle_quantiser_bitwise(d, dff):
     inp["wg"][:, 3] = 0
     inp["wu"][:, 5] = 0
     inp["wu"][7, 1] = wl.f32_to_bf16_bits(np.array([50.0], dtype=np.float32))[0]
+    # non-finite weights: a NaN (code 0x7F, no effect on the scale), a NaN in
+    # an otherwise zero column (scale 0, code 0), -inf (infinite scale)
+    inp["wg"][2, 4] = 0x7FC0
+    inp["wu"][:, 7] = 0
+    inp["wu"][3, 7] = 0x7FC0
+    inp["wg"][9, 6] = 0xFF80
+    inp["wd"][5, 2] = 0x7FC0
     wp, wdp = pack(inp, d, dff, W8)
     buf = wp.cpu().numpy()
     (qg, sg), (qu, su) = unpack_fp8(buf, d, dff, plain=False)

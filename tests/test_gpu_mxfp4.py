@@ -44,6 +44,14 @@ def test_pack_matches_the_oracle_quantiser_bitwise(d, dff):
     inp["wg"][:, 3] = 0                          # all-zero blocks
     inp["wu"][:40, 5] = 0
     inp["wu"][7, 1] = wl.f32_to_bf16_bits(np.array([50.0], dtype=np.float32))[0]
+    # non-finite weights: NaN and infinities are coded +-6, a NaN does not
+    # count toward its block's exponent (also in an otherwise zero block),
+    # an infinity puts it at the top
+    inp["wg"][2, 4] = 0x7FC0
+    inp["wu"][:, 7] = 0
+    inp["wu"][3, 7] = 0xFFC0
+    inp["wg"][40, 6] = 0xFF80
+    inp["wd"][5, 2] = 0x7F80
     wp, wdp = pack(inp, d, dff, W4)
     (qg, sg), (qu, su) = unpack_mxfp4(wp.cpu().numpy(), d, dff, plain=False)
     nbk = -(-d // 32)

@@ -47,8 +47,8 @@ MUTANTS = {
     "e2m1_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e - 2)"),
     "e2m1_ties_away": ("nearbyint(a / step) * step", "round(a / step) * step"),
     "mx_exponent_offset": ("int s = (e - 1) - 2;", "int s = (e - 1) - 3;"),
-    "mx_zero_block": ("    if (amax == 0.0)\n        return 0;\n    int e;",
-                      "    if (amax == 0.0)\n        return -126;\n    int e;"),
+    "mx_zero_block": ("    if (amax == 0.0 || isnan(amax))\n        return 0;",
+                      "    if (amax == 0.0 || isnan(amax))\n        return -126;"),
     "mx_unscaled_codes": ("oracle_e2m1_from_double(ldexp(oracle_bf16_to_double(w[k * N + n]), -s))",
                           "oracle_e2m1_from_double(oracle_bf16_to_double(w[k * N + n]))"),
     "mx_first_block_scale": ("(int)scales[(k / 32) * N + n] - 127", "(int)scales[n] - 127"),

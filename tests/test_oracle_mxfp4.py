@@ -54,6 +54,27 @@ def test_e2m1_ties_to_even_and_saturation(v, code):
     assert oracle.e2m1_from_double(v) == code
 
 
+def test_non_finite_values_saturate_with_their_sign():
+    # E2M1's value table has no infinity or NaN: the reading taken is that
+    # they lie beyond 6 and saturate, keeping the sign bit
+    assert oracle.e2m1_from_double(math.inf) == 7
+    assert oracle.e2m1_from_double(-math.inf) == 15
+    assert oracle.e2m1_from_double(math.nan) == 7
+    assert oracle.e2m1_from_double(-math.nan) == 15
+    # floor(log2(inf)) - 2 is infinite: the clamp's top
+    assert oracle.mx_shared_exponent(math.inf) == 127
+
+
+def test_nan_weight_does_not_set_the_block_exponent():
+    w = wl.f32_to_bf16_bits(np.full((40, 2), 1.0, dtype=np.float32))
+    w[5, 0] = 0x7FC0                        # NaN among ones
+    w[:, 1] = 0
+    w[33, 1] = 0xFF80                       # -inf alone in the ragged block
+    q, sc = oracle.quantize_mxfp4(w)
+    assert sc[0, 0] == 127 - 2 and q[5, 0] == 7 and q[4, 0] == 6   # 1.0 = 4 * 2^-2, code 6
+    assert sc[1, 1] == 127 + 127 and q[33, 1] == 15 and sc[0, 1] == 127
+
+
 def test_shared_exponent_puts_the_block_max_in_4_to_8():
     rng = np.random.default_rng(3)
     for amax in np.exp2(rng.uniform(-100, 100, 500)):
