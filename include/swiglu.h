@@ -250,7 +250,8 @@ int swiglu_up_noalloc(const void *x, const void *Wpacked, void *out,
 
 /*
  * y (M x d) = (silu(x . Wgate) (.) (x . Wup)) . Wdown: the MLP of the layer
- * skeleton, with Wpacked from swiglu_pack_weights and Wdpacked from
+ * skeleton ("Anatomie d'un transformeur sur GPU" §1.1: Wgate and Wup into
+ * SwiGLU, then Wdown), with Wpacked from swiglu_pack_weights and Wdpacked from
  * swiglu_pack_down.  The intermediate h (M x dff) is kept in the workspace
  * in the storage dtype (bf16 or fp32), then multiplied by Wdown with fp32
  * accumulation.
@@ -259,7 +260,8 @@ int mlp_forward(const void *x, const void *Wpacked, const void *Wdpacked, void *
                 int64_t M, int64_t d, int64_t dff, int dtype,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* mlp_forward with a forced path for both products. */
+/* mlp_forward (the MLP of "Anatomie d'un transformeur sur GPU" §1.1) with a
+ * forced path for both products. */
 int mlp_forward_ex(const void *x, const void *Wpacked, const void *Wdpacked, void *y,
                    int64_t M, int64_t d, int64_t dff, int dtype,
                    void *workspace, size_t workspace_bytes, hipStream_t stream, int path);
