@@ -250,7 +250,10 @@ def test_header_is_plain_c_and_links(tmp_path):
     cmd[cmd.index("-L") + 1] = str(tmp_path)
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
-    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    # every GPU hidden from the program (HIP reports no device), so a call
+    # that wrongly passed validation could not launch on a placeholder address
+    env = dict(os.environ, ROCR_VISIBLE_DEVICES="", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60, env=env)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "abi_check ok" in r.stdout
 

@@ -10,7 +10,11 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1")
+# every GPU hidden from the drivers (HIP then reports no device): their calls
+# are all rejected before any launch, and if a change ever let one through
+# it fails on the host instead of reaching a GPU with a placeholder address
+ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1",
+           ROCR_VISIBLE_DEVICES="", HIP_VISIBLE_DEVICES="")
 
 
 def _run(exe, marker):
