@@ -476,7 +476,8 @@ static int bf16_row_tiles(int64_t M) {
 
 // Pair blocks per wave of the bf16 kernel with bf16 weights: two once x's
 // fragment is as large as a weight piece (more than 8 rows), one otherwise.
-// For FP8 and MXFP4 weights pick_mt_bf16 sets the count by row range and
+// pick_mt_bf16 overrides it for a gate/up product of 3 to 16 rows (two or
+// four), and for FP8 and MXFP4 weights sets the count by row range and
 // product (FP8 planned as two).
 static int bf16_pair_blocks(int64_t M, int dt) {
     return (dt == DT_FP8W || M > 8) ? 2 : 1;
@@ -612,11 +613,17 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // us, 72B-class MLP at 16 rows 225.7 -> 219.0 us; eight waves, or
             // four pieces in flight, were slower); with the pipelined loop
             // one piece per half and step (38.4 -> 37.6 us; two: 38.4).
-            // Above two rows four pieces per half (8B-class at 4 rows 38.3
-            // -> 37.8 us pipelined; eight there: 38.8), up to two rows
-            // eight (37.3 us; four: 38.0)
+            // From three to eight rows a gate/up product takes two pair
+            // blocks per wave, one piece per half and step (8B-class at 4
+            // and 8 rows 37.4, 38.2 -> 36.7-36.8, 37.2-37.3 us; at one row
+            // the same shape gains nothing, and at 16 rows it is slower:
+            // 37.2 -> 39.0 us).  Other products above two rows: four pieces
+            // per half (8B-class at 4 rows 38.3 -> 37.8 us pipelined;
+            // eight there: 38.8); up to two rows eight (37.3 us; four: 38.0)
             if (g.M > 8 && EPI == EPI_SWIGLU)
                 pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
+            else if (g.M > 2 && EPI == EPI_SWIGLU)
+                pick_split_bf16<1, 1, 2, EPI, WF>(g, p, partial, s);
             else if (p.pb_per_wg == 2)
                 pick_split_bf16<1, 4, 2, EPI, WF>(g, p, partial, s);
             else if (g.M > 2)
