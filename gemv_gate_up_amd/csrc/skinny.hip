@@ -476,8 +476,8 @@ static int bf16_row_tiles(int64_t M) {
 
 // Pair blocks per wave of the bf16 kernel with bf16 weights: two once x's
 // fragment is as large as a weight piece (more than 8 rows), one otherwise.
-// pick_mt_bf16 overrides it for a gate/up product of 3 to 16 rows (two or
-// four), and for FP8 and MXFP4 weights sets the count by row range and
+// pick_mt_bf16 overrides it for some gate/up products of 3 to 16 rows (two
+// or four), and for FP8 and MXFP4 weights sets the count by row range and
 // product (FP8 planned as two).
 static int bf16_pair_blocks(int64_t M, int dt) {
     return (dt == DT_FP8W || M > 8) ? 2 : 1;
@@ -555,6 +555,7 @@ static void pick_split_bf16(const GemmArgs& g, const SkinnyPlan& p, float* parti
 // fragments (times two with FP8 weights), measured on the 8B- and
 // 72B-class decode shapes.
 constexpr int64_t MXFP4_WIDE_PB_CUS = 256;   // MI355X compute units
+constexpr int64_t SKINNY_CUS = 256;          // the same, for the bf16 shape choices
 
 template <int EPI, int WF>
 static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
@@ -613,16 +614,20 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // us, 72B-class MLP at 16 rows 225.7 -> 219.0 us; eight waves, or
             // four pieces in flight, were slower); with the pipelined loop
             // one piece per half and step (38.4 -> 37.6 us; two: 38.4).
-            // From three to eight rows a gate/up product takes two pair
-            // blocks per wave, one piece per half and step (8B-class at 4
-            // and 8 rows 37.4, 38.2 -> 36.7-36.8, 37.2-37.3 us; at one row
-            // the same shape gains nothing, and at 16 rows it is slower:
-            // 37.2 -> 39.0 us).  Other products above two rows: four pieces
-            // per half (8B-class at 4 rows 38.3 -> 37.8 us pipelined;
-            // eight there: 38.8); up to two rows eight (37.3 us; four: 38.0)
+            // From three to eight rows, a gate/up product of 2 to 4 pair
+            // blocks per CU takes two pair blocks per wave, one piece per
+            // half and step (8B-class, 896 pair blocks, at 4 and 8 rows
+            // 37.4, 38.2 -> 36.7-36.8, 37.2-37.3 us).  Outside that range it
+            // was slower: 304 pair blocks (0.5B-class) 5.8, 6.0 -> 6.9,
+            // 6.8 us; 1,848 (72B-class) 143.8, 145.0 -> 145.3, 145.8 us.  At
+            // one row it gains nothing, and at 16 rows it is slower (37.2 ->
+            // 39.0 us).  Other products above two rows: four pieces per half
+            // (8B-class at 4 rows 38.3 -> 37.8 us pipelined; eight there:
+            // 38.8); up to two rows eight (37.3 us; four: 38.0)
             if (g.M > 8 && EPI == EPI_SWIGLU)
                 pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
-            else if (g.M > 2 && EPI == EPI_SWIGLU)
+            else if (g.M > 2 && EPI == EPI_SWIGLU && p.grid_pb >= 2 * SKINNY_CUS &&
+                     p.grid_pb <= 4 * SKINNY_CUS)
                 pick_split_bf16<1, 1, 2, EPI, WF>(g, p, partial, s);
             else if (p.pb_per_wg == 2)
                 pick_split_bf16<1, 4, 2, EPI, WF>(g, p, partial, s);
