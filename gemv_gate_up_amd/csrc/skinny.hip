@@ -564,6 +564,13 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // MXFP4 activation fragments (4 per piece and row tile) bound U above
     // two row tiles
     constexpr bool Q = WF != WF_BF16;
+    // Four pair blocks per workgroup leave a small gate/up product (the
+    // 0.5B-class shape: 304 pair blocks, 76 workgroups) on under half the
+    // CUs; such products take two per workgroup above 8 rows (0.5B-class
+    // at 16 rows: bf16 9.0 -> 6.5 us, its MLP 16.7 -> 14.1 us; FP8 weights
+    // 7.2 -> 5.3 us, MXFP4 6.1 -> 4.7 us; the 8B-class shape and the
+    // 72B-class tensor-parallel shard, 224 and 232 workgroups, keep four).
+    const bool few4 = EPI == EPI_SWIGLU && ceil_div(p.grid_pb, 4) * p.splits < SKINNY_CUS / 2;
     switch (p.row_tile / 16) {
     case 1:
         if constexpr (WF == WF_MXFP4) {
@@ -580,6 +587,8 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // on eight waves (8B-class at 16 rows 15.8 -> 15.5 us)
             if (g.M > 8 && p.grid_pb >= 4 * MXFP4_WIDE_PB_CUS)
                 pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
+            else if (g.M > 8 && few4)
+                pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else if (g.M > 8 && EPI == EPI_SWIGLU)
                 pick_split_bf16<1, 1, 4, EPI, WF, 8>(g, p, partial, s);
             else if (g.M <= 4 || (EPI == EPI_PLAIN && g.M > 8))
@@ -603,6 +612,8 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
                 pick_split_bf16<1, 2, 1, EPI, WF, 8>(g, p, partial, s);
             else if (EPI == EPI_PLAIN && g.M > 8)
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
+            else if (g.M > 8 && few4)
+                pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else if (g.M > 8)
                 pick_split_bf16<1, 1, 4, EPI, WF, 8>(g, p, partial, s);
             else
@@ -624,7 +635,9 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // 39.0 us).  Other products above two rows: four pieces per half
             // (8B-class at 4 rows 38.3 -> 37.8 us pipelined; eight there:
             // 38.8); up to two rows eight (37.3 us; four: 38.0)
-            if (g.M > 8 && EPI == EPI_SWIGLU)
+            if (g.M > 8 && few4)
+                pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
+            else if (g.M > 8 && EPI == EPI_SWIGLU)
                 pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
             else if (g.M > 2 && EPI == EPI_SWIGLU && p.grid_pb >= 2 * SKINNY_CUS &&
                      p.grid_pb <= 4 * SKINNY_CUS)
