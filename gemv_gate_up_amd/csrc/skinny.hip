@@ -571,6 +571,12 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // 7.2 -> 5.3 us, MXFP4 6.1 -> 4.7 us; the 8B-class shape and the
     // 72B-class tensor-parallel shard, 224 and 232 workgroups, keep four).
     const bool few4 = EPI == EPI_SWIGLU && ceil_div(p.grid_pb, 4) * p.splits < SKINNY_CUS / 2;
+    // Likewise up to 8 rows with FP8 and MXFP4 weights: where two pair
+    // blocks per workgroup would give fewer workgroups than CUs, one (the
+    // 0.5B-class shape at 1, 4 and 8 rows: MXFP4 4.1, 4.2, 4.7 -> 3.9,
+    // 4.05, 4.3 us; FP8 at 4 and 8 rows 5.4, 5.6 -> 4.7, 5.0 us; the 8B-
+    // and 72B-class shapes unchanged).
+    const bool few2 = EPI == EPI_SWIGLU && ceil_div(p.grid_pb, 2) * p.splits < SKINNY_CUS;
     switch (p.row_tile / 16) {
     case 1:
         if constexpr (WF == WF_MXFP4) {
@@ -591,8 +597,12 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else if (g.M > 8 && EPI == EPI_SWIGLU)
                 pick_split_bf16<1, 1, 4, EPI, WF, 8>(g, p, partial, s);
+            else if (g.M <= 4 && few2)
+                pick_split_bf16<1, 1, 1, EPI, WF, 8>(g, p, partial, s);
             else if (g.M <= 4 || (EPI == EPI_PLAIN && g.M > 8))
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
+            else if (few2)
+                pick_split_bf16<1, 1, 1, EPI, WF, 8>(g, p, partial, s);
             else
                 pick_split_bf16<1, 1, 2, EPI, WF>(g, p, partial, s);
         } else if constexpr (Q) {
@@ -616,6 +626,8 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else if (g.M > 8)
                 pick_split_bf16<1, 1, 4, EPI, WF, 8>(g, p, partial, s);
+            else if (few2)
+                pick_split_bf16<1, 2, 1, EPI, WF, 8>(g, p, partial, s);
             else
                 pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
         } else {
