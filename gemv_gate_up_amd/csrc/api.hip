@@ -29,9 +29,12 @@ namespace {
 constexpr int64_t MAX_DIM = (int64_t)1 << 20;
 constexpr int64_t MAX_M = (int64_t)1 << 18;
 // skinny/wide crossover, measured with both paths forced: skinny wins up to
-// 80 rows on the 8B-class shape, wide from 64 rows on the 72B-class shape
+// 80 rows on the 8B-class shape, wide from 64 rows on the 72B-class shape;
+// above it the wide path still needs enough workgroups (resolve_path)
 constexpr int64_t SKINNY_MAX_M_BF16 = 64;
 constexpr int TARGET_CUS = 256;   // MI355X compute units: split-K planning target
+// From 256 rows on the wide path wins with fewer workgroups (see resolve_path)
+constexpr int64_t WIDE_MIN_TILES_256 = 48;
 constexpr size_t WS_ALIGN = 256;
 
 size_t align_up(size_t v) { return (v + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
@@ -103,8 +106,20 @@ int resolve_path(const GemmArgs& g, int path)
         return wide_supported(g) ? SWIGLU_PATH_WIDE : SWIGLU_ERR_UNSUPPORTED;
     if (path == SWIGLU_PATH_SKINNY)
         return SWIGLU_PATH_SKINNY;
-    if (g.dt == DT_BF16 && g.M > SKINNY_MAX_M_BF16 && wide_supported(g))
-        return SWIGLU_PATH_WIDE;
+    if (g.dt == DT_BF16 && g.M > SKINNY_MAX_M_BF16 && wide_supported(g)) {
+        // The wide path needs a grid that keeps the chip busy.  A small
+        // matrix gives it few tiles (the 0.5B-class gate/up product 76 up
+        // to 256 rows, a down product into d = 896 only 8 to 16), and the
+        // split-over-weights kernels, which re-read the weights once per 64
+        // rows, are then faster: forced-path sweeps over 0.5B-, 1.5B-, 3B-
+        // and 8B-class shapes and a 72B tensor-parallel shard, 80 to 1024
+        // rows, found the wide path faster wherever its grid held at least
+        // 128 workgroups, or at least 48 from 256 rows on, and slower
+        // elsewhere but for one case (the shard's down product at 128 rows).
+        const int64_t tiles = wide_grid_tiles(g);
+        if (tiles >= TARGET_CUS / 2 || (g.M >= 256 && tiles >= WIDE_MIN_TILES_256))
+            return SWIGLU_PATH_WIDE;
+    }
     return SWIGLU_PATH_SKINNY;
 }
 

@@ -83,6 +83,8 @@ hipError_t launch_wide(const GemmArgs& g, hipStream_t s);
 // Two-pass (gate K loop, then up K loop) schedule; gate/up products only.
 hipError_t launch_wide_phased(const GemmArgs& g, hipStream_t s);
 int wide_supported(const GemmArgs& g);
+// Workgroups the wide launch of this product would use (for the dispatcher).
+int64_t wide_grid_tiles(const GemmArgs& g);
 // Sets the launch attributes of every wide instantiation (host calls only);
 // done before a stream capture so that none of them is recorded inside it.
 hipError_t wide_prepare();

@@ -82,6 +82,22 @@ hipError_t wide_prepare()
     return e;
 }
 
+// Workgroups of the grid launch_wide_epi runs for this product: the 256 x
+// 256 tiles, or as many narrower tiles when those would fill at most half
+// the compute units (its tail split leaves the count above that unchanged
+// for the dispatcher's purpose).
+int64_t wide_grid_tiles(const GemmArgs& g)
+{
+    using C = WideCfg;
+    using T = WideTailCfg;
+    using H = WideHalfCfg;
+    const int64_t G = wide_full_grid<C::BM, C::BN, C::BN / 32>(g).blocks;
+    if (G > WIDE_CUS / 2)
+        return G;
+    return g.M <= T::BM ? wide_full_grid<T::BM, T::BN, T::BN / 32>(g).blocks
+                        : wide_full_grid<H::BM, H::BN, H::BN / 32>(g).blocks;
+}
+
 template <int EPI>
 static hipError_t launch_wide_epi(const GemmArgs& g, hipStream_t s)
 {

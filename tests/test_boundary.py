@@ -62,6 +62,14 @@ def test_dispatcher():
         assert sw.swiglu_select_path(M, 4096, 14336, BF16) == sw.SWIGLU_PATH_SKINNY
     for M in (65, 128, 2048, 4096):
         assert sw.swiglu_select_path(M, 4096, 14336, BF16) == sw.SWIGLU_PATH_WIDE
+    # above 64 rows the wide path needs enough workgroups: at least 128, or
+    # 48 from 256 rows on.  The 0.5B-class gate/up product has 76 up to 256
+    # rows and 152 at 512; the 72B-class shard (d_ff = 3696) 58 up to 256
+    # rows; the 1.5B-class product (d_ff = 8960) 140 at 80 rows
+    for M, d, dff, path in ((80, 896, 4864, 1), (128, 896, 4864, 1), (255, 896, 4864, 1),
+                            (256, 896, 4864, 2), (512, 896, 4864, 2), (128, 8192, 3696, 1),
+                            (256, 8192, 3696, 2), (80, 1536, 8960, 2)):
+        assert sw.swiglu_select_path(M, d, dff, BF16) == path, (M, d, dff)
     for M in (1, 64, 4096):
         assert sw.swiglu_select_path(M, 512, 2048, F32) == sw.SWIGLU_PATH_SKINNY
     assert sw.swiglu_select_path(1, 4096, 14336, 9) == sw.SWIGLU_ERR_UNSUPPORTED
@@ -267,9 +275,12 @@ def _al(n):
     return -(-n // 256) * 256
 
 
-@pytest.mark.parametrize("shape", [(4096, 4096, 14336), (2048, 8192, 29568), (130, 264, 712)])
+# the last shape is ragged in M, d and dff, with both products still on the
+# wide path (108 and 50 workgroups at 300 rows)
+@pytest.mark.parametrize("shape", [(4096, 4096, 14336), (2048, 8192, 29568), (300, 3080, 3400)])
 def test_packed_plan_workspace_formulas(shape):
     M, d, dff = shape
+    assert sw.swiglu_select_path(M, d, dff, BF16) == sw.SWIGLU_PATH_WIDE
     # swiglu_up on the many-rows path: packed x only
     assert sw.swiglu_workspace_bytes(M, d, dff, BF16, 0) == _al(_packed_bytes(M, d))
     # mlp_forward: h packed for the down product, then packed x (no split-K partials)
@@ -283,7 +294,7 @@ def test_packed_plan_workspace_formulas(shape):
 def test_workspace_below_the_row_major_plan_is_rejected():
     # the row-major plan of mlp_forward keeps h as M x padded-dff bf16; one
     # allocation unit less than that fails before any launch
-    M, d, dff = 256, 512, 1408
+    M, d, dff = 300, 3080, 3400   # both products on the wide path
     row_major = _al(M * (-(-dff // 128) * 128) * 2)
     assert sw.swiglu_workspace_bytes(M, d, dff, BF16, 1) > row_major
     rejected_before_launch(

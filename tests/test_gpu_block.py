@@ -53,6 +53,7 @@ def _reference(inp, dtype, bias=True):
 CASES = [
     (1, 256, 512, BF16, 0), (7, 136, 392, BF16, 0), (64, 896, 4864, BF16, 0),
     (130, 264, 712, BF16, 0), (300, 1000, 1400, BF16, 0), (96, 512, 1408, BF16, 1),
+    (130, 264, 712, BF16, 2), (300, 1000, 1400, BF16, 2),
     (4, 100, 60, F32, 0), (12, 64, 520, F32, 0),
     (16, 1032, 776, W8, 0), (64, 896, 4864, W8, 0),
     (16, 1032, 776, W4, 0), (64, 896, 4864, W4, 0),
@@ -70,14 +71,15 @@ def test_block_matches_oracle(case, bias):
     assert_close(out, _reference(inp, dtype, bias), dtype, "block %s" % (case,))
 
 
-@pytest.mark.parametrize("case", [(16, 1024, 1408, BF16), (300, 1000, 1400, BF16),
-                                  (1, 512, 2048, F32), (16, 1032, 776, W8)])
+@pytest.mark.parametrize("case", [(16, 1024, 1408, BF16, 0), (300, 1000, 1400, BF16, 0),
+                                  (300, 1000, 1400, BF16, 2), (1, 512, 2048, F32, 0),
+                                  (16, 1032, 776, W8, 0)])
 def test_block_in_place_equals_out_of_place(case):
-    M, d, dff, dtype = case
+    M, d, dff, dtype, path = case
     inp = _block_inputs(3 * M + d, M, d, dff, dtype)
     wp, wdp = pack(inp, d, dff, dtype)
-    a = _run(inp, wp, wdp, M, d, dff, dtype).cpu().numpy()
-    b = _run(inp, wp, wdp, M, d, dff, dtype, inplace=True).cpu().numpy()
+    a = _run(inp, wp, wdp, M, d, dff, dtype, path=path).cpu().numpy()
+    b = _run(inp, wp, wdp, M, d, dff, dtype, path=path, inplace=True).cpu().numpy()
     assert np.array_equal(a, b)
 
 

@@ -13,7 +13,7 @@ from swiglu_testlib import assert_close, bytes_buf, dev, empty, host, pack, say,
 pytestmark = pytest.mark.gpu
 
 BF16, F32 = wl.BF16, wl.F32
-AUTO, PHASED = sw.SWIGLU_PATH_AUTO, sw.SWIGLU_PATH_WIDE_PHASED
+AUTO, WIDE, PHASED = sw.SWIGLU_PATH_AUTO, sw.SWIGLU_PATH_WIDE, sw.SWIGLU_PATH_WIDE_PHASED
 FUSED = sw.SWIGLU_PATH_FUSED_DOWN
 
 # (M, d, dff, dtype, with_down, path): split-K skinny with its reduce kernel,
@@ -24,8 +24,8 @@ CASES = [
     (1, 512, 2048, F32, False, AUTO),
     (64, 896, 4864, BF16, True, AUTO),
     (16, 1024, 1408, BF16, True, AUTO),
-    (300, 1000, 1400, BF16, False, AUTO),
-    (130, 264, 712, BF16, True, AUTO),
+    (300, 1000, 1400, BF16, False, WIDE),
+    (130, 264, 712, BF16, True, WIDE),
     (257, 520, 2056, BF16, False, PHASED),
     (64, 896, 4864, BF16, True, FUSED),
     (20, 1032, 776, BF16, True, FUSED),
@@ -128,7 +128,10 @@ def test_empty_batch_records_an_empty_graph():
         sw.swiglu_graph_destroy(g)
 
 
-@pytest.mark.parametrize("case", [(16, 1024, 1408, BF16), (130, 264, 712, BF16)])
+# skinny products; skinny products at 130 rows; both products on the wide
+# path (300 rows, 108 and 50 workgroups)
+@pytest.mark.parametrize("case", [(16, 1024, 1408, BF16), (130, 264, 712, BF16),
+                                  (300, 3080, 3400, BF16)])
 def test_block_graph_replays_equal_the_direct_call(case):
     M, d, dff, dtype = case
     torch = torch_mod()

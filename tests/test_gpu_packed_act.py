@@ -93,8 +93,13 @@ def test_block_packed_and_in_place_agree(shape):
 
 
 def test_too_small_workspace_is_still_rejected():
+    # both products of this shape take the wide path (108 and 50 workgroups
+    # at 300 rows), whose packed plan needs more than the row-major h; every
+    # plan of an MLP needs at least that h, so less is rejected before any
+    # launch (the weights here are placeholders of 16 bytes)
     sw = sw_mod()
-    M, d, dff = 256, 512, 1408
+    M, d, dff = 300, 3080, 3400
+    assert sw.swiglu_select_path(M, d, dff, BF16) == sw.SWIGLU_PATH_WIDE
     nb = sw.swiglu_workspace_bytes(M, d, dff, BF16, 1)
     row_major_h = M * (-(-dff // 128) * 128) * 2
     assert nb > row_major_h

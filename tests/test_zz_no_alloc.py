@@ -36,8 +36,9 @@ CASES = [
     ("split-K bf16", wl.BF16, 8192, 1024, 16, 3),
     # few rows, no split: the array is not touched
     ("decode bf16", wl.BF16, 1024, 2816, 4, 1),
-    # many rows: x packed into the array (ragged rows and K)
-    ("wide packed x", wl.BF16, 1000, 1400, 300, 97),
+    # many rows: x packed into the array (ragged rows and K; a d_ff whose
+    # grid keeps both calls on the wide path)
+    ("wide packed x", wl.BF16, 1000, 8200, 300, 97),
     # many rows whose packed x exceeds the array: x read in place
     ("wide in place", wl.BF16, 4096, 512, 4608, 129),
 ]
