@@ -483,7 +483,16 @@ static int bf16_pair_blocks(int64_t M, int dt) {
     return (dt == DT_FP8W || M > 8) ? 2 : 1;
 }
 
-static int f32_row_tile(int64_t M) {
+// Rows per fp32 workgroup.  Above 8 rows, 16 when the pair blocks alone
+// give at least two workgroups per CU: the weights are then read once per
+// 16 rows instead of 8 (8B-class at 12, 16 and 64 rows 201, 225, 786 ->
+// 171, 201, 691 us with four pieces in flight; eight, 166, 193, 649 us,
+// spill two scalar registers); a smaller matrix keeps 8 and so twice the
+// workgroups (0.5B-class, 304 pair blocks, at 16 rows: 22.5 us, 27.4-29.1
+// with 16).
+static int f32_row_tile(int64_t M, int64_t grid_pb, int num_cus) {
+    if (M > 8 && grid_pb >= 2 * (int64_t)num_cus)
+        return 16;
     return M >= 8 ? 8 : (M > 2 ? 4 : (M == 2 ? 2 : 1));
 }
 
@@ -494,7 +503,7 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
     p.pb_per_wg = g.dt != DT_F32 ? bf16_pair_blocks(g.M, g.dt) : 1;
     if (g.dt != DT_F32 && g.epi == EPI_PLAIN && g.M > 16)
         p.pb_per_wg = 1;
-    p.row_tile = g.dt != DT_F32 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M);
+    p.row_tile = g.dt != DT_F32 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M, p.grid_pb, num_cus);
     p.row_groups = ceil_div(g.M, p.row_tile);
     // Split K only when there are too few pair blocks (units of weight
     // streaming) to keep every CU busy; two pair blocks per workgroup are
@@ -703,6 +712,12 @@ static void pick_rt_f32(const GemmArgs& g, const SkinnyPlan& p, float* partial, 
     case 1: pick_split_f32<1, EPI>(g, p, partial, s); break;
     case 2: pick_split_f32<2, EPI>(g, p, partial, s); break;
     case 4: pick_split_f32<4, EPI>(g, p, partial, s); break;
+    case 16:   // four pieces in flight (see f32_row_tile)
+        if (p.splits > 1)
+            go_f32<16, 4, EPI, true>(g, p, partial, s);
+        else
+            go_f32<16, 4, EPI, false>(g, p, partial, s);
+        break;
     default: pick_split_f32<8, EPI>(g, p, partial, s); break;
     }
 }

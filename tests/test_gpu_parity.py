@@ -89,7 +89,10 @@ def test_up_bf16_random(shape, path):
     assert_close(out, ref, BF16, "up bf16 %s path %d" % (shape, path))
 
 
-F32_SHAPES = [(1, 512, 2048), (2, 36, 20), (5, 100, 60), (9, 260, 132), (33, 64, 2048)]
+# the last two take 16-row tiles (at least 512 pair blocks above 8 rows): a
+# partial tile of 12 rows, and 20 rows as one full tile and a partial one
+F32_SHAPES = [(1, 512, 2048), (2, 36, 20), (5, 100, 60), (9, 260, 132), (33, 64, 2048),
+              (12, 520, 8200), (20, 264, 8200)]
 
 
 @pytest.mark.parametrize("shape", F32_SHAPES)
@@ -104,7 +107,8 @@ def test_up_f32_random(shape):
 
 
 MLP_SHAPES = [(1, 256, 512, BF16), (7, 136, 392, BF16), (64, 896, 4864, BF16),
-              (130, 264, 712, BF16), (4, 100, 60, F32), (12, 64, 520, F32)]
+              (130, 264, 712, BF16), (4, 100, 60, F32), (12, 64, 520, F32),
+              (20, 264, 8200, F32)]
 
 
 @pytest.mark.parametrize("shape", MLP_SHAPES)
