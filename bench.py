@@ -62,6 +62,7 @@ MARKER_NAME = "FillFunctor"    # torch's fill kernel: the markers' kernel name c
 COMMON_SOURCES = ["geometry.h", "device_common.h", "launch.h", "api.hip"]
 FAMILY_SOURCES = {
     "skinny_bf16_kernel": ["skinny.hip"], "skinny_f32_kernel": ["skinny.hip"],
+    "skinny_f32m_kernel": ["skinny.hip"],
     "splitk_reduce_kernel": ["skinny.hip"], "wide_bf16_kernel": ["wide.hip", "wide_kernel.h"],
     "pack_act_kernel": ["pack.hip"], "rmsnorm_kernel": ["norm.hip"],
     "mlp_fused_kernel": ["fused.hip"],
@@ -326,7 +327,9 @@ def dominant_kernel(w: wl.Workload, path: int) -> str:
         return "mlp_fused_kernel"
     if path in (2, 3):
         return "wide_bf16_kernel"
-    return "skinny_f32_kernel" if w.dtype == wl.F32 else "skinny_bf16_kernel"
+    if w.dtype == wl.F32:   # the VALU kernel up to two rows, the matrix unit above
+        return "skinny_f32_kernel" if w.M <= 2 else "skinny_f32m_kernel"
+    return "skinny_bf16_kernel"
 
 
 def block_bytes(w: wl.Workload) -> int:

@@ -287,6 +287,139 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
     }
 }
 
+// ---------------------------------------------------------------- fp32 (matrix)
+// fp32 on the matrix unit, v_mfma_f32_16x16x4_f32, from the fp32 piece
+// layout: lane l holds column l % 16 and the four consecutive K values
+// 4 (l / 16) .. 4 (l / 16) + 3 of the piece's 16.  MFMA j takes K value
+// 4 (l / 16) + j as its k index l / 16 for both operands, so the four MFMAs
+// of a piece sum all 16, and one 16-byte activation load per lane and row
+// tile (row l % 16, the same four K values) feeds them.  Same decomposition,
+// combine and epilogue as skinny_bf16_kernel; the VALU kernel below keeps
+// one row, where a 16-row MFMA would waste most of its work.
+template <int MT, int U, int NPB, int EPI, bool SPLIT, int NWV>
+__global__ void __launch_bounds__(NWV * 64)
+skinny_f32m_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
+                   const f32x4* __restrict__ w, int64_t nkc, int64_t cps,
+                   float* __restrict__ out, int64_t ldo, int64_t ncols_out,
+                   float* __restrict__ partial, int64_t npc, int M,
+                   const float* __restrict__ resid, int64_t ldr, const float* __restrict__ bias)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t pb0 = (int64_t)blockIdx.x * NPB;
+    const int s = blockIdx.y;
+    const int rbase = blockIdx.z * 16 * MT;
+    const int64_t kbeg = (int64_t)s * cps;
+    const int64_t kend = kbeg + cps < nkc ? kbeg + cps : nkc;
+    const f32x4* wp = w + pb0 * nkc * 2 * PIECE_VECS + lane;
+    const int arow = lane & 15;
+    const int akoff = (lane >> 4) * 4;
+
+    f32x4 accg[NPB][MT], accu[NPB][MT];
+#pragma unroll
+    for (int p = 0; p < NPB; ++p)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            accg[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accu[p][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+    for (int64_t kb = kbeg + wave; kb < kend; kb += NWV * U) {
+        f32x4 wg[NPB][U], wu[NPB][U], xa[U][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kc = kb + NWV * u;
+#pragma unroll
+            for (int p = 0; p < NPB; ++p) {
+                if (kc < kend) {
+                    wg[p][u] = __builtin_nontemporal_load(wp + (p * nkc * 2 + kc * 2) * PIECE_VECS);
+                    wu[p][u] = __builtin_nontemporal_load(wp + (p * nkc * 2 + kc * 2 + 1) * PIECE_VECS);
+                } else {
+                    wg[p][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    wu[p][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kc = kb + NWV * u;
+            const int64_t k = kc * 16 + akoff;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int row = rbase + mt * 16 + arow;
+                xa[u][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (kc < kend && row < M && k < kvalid)
+                    xa[u][mt] = *(const f32x4*)(a + (int64_t)row * lda + k);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int p = 0; p < NPB; ++p)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        accg[p][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            xa[u][mt][j], wg[p][u][j], accg[p][mt], 0, 0, 0);
+                        accu[p][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            xa[u][mt][j], wu[p][u][j], accu[p][mt], 0, 0, 0);
+                    }
+    }
+
+    // Combine the waves in LDS, in wave order, as skinny_bf16_kernel does;
+    // lane l holds rows 4 (l / 16) + i (i = 0..3) of column l % 16.
+    __shared__ float red[NWV][MT][2][64 * 4];
+    const int t = threadIdx.x;
+    const int r = t >> 4, c = t & 15;
+    const int src = ((r >> 2) * 16 + c) * 4 + (r & 3);
+#pragma unroll
+    for (int p = 0; p < NPB; ++p) {
+        const int64_t pb = pb0 + p;
+        if (p > 0)
+            __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                red[wave][mt][0][lane * 4 + i] = accg[p][mt][i];
+                red[wave][mt][1][lane * 4 + i] = accu[p][mt][i];
+            }
+        }
+        __syncthreads();
+        if (NWV > 4 && t >= 256)
+            continue;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float g = 0.f, u = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < NWV; ++wv) {
+                g += red[wv][mt][0][src];
+                u += red[wv][mt][1][src];
+            }
+            const int row = rbase + mt * 16 + r;
+            if (row >= M)
+                continue;
+            if (SPLIT) {
+                float* pr = partial + ((int64_t)s * M + row) * npc + pb * 32;
+                pr[c] = g;
+                pr[16 + c] = u;
+            } else if (EPI == EPI_SWIGLU) {
+                const int64_t n = pb * 16 + c;
+                if (n < ncols_out)
+                    store_out(out + (int64_t)row * ldo + n, silu(g) * u);
+            } else {
+                const int64_t j = pb * 32 + c;
+                if (j < ncols_out)
+                    store_out(out + (int64_t)row * ldo + j, plain_tail(g, resid, ldr, bias, row, j));
+                if (j + 16 < ncols_out)
+                    store_out(out + (int64_t)row * ldo + j + 16,
+                              plain_tail(u, resid, ldr, bias, row, j + 16));
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- fp32 (VALU)
 // Lane l covers column l % 16 and k-group l / 16 (4 consecutive K values)
 // of each piece; the four k-groups are added with two butterfly steps whose
@@ -469,6 +602,14 @@ splitk_reduce_kernel(const float* __restrict__ partial, int S, int M, int64_t np
 }
 
 // ---------------------------------------------------------------- planning
+// fp32 calls of at least this many rows take the matrix-unit kernel
+// (skinny_f32m_kernel), fewer the VALU kernel.  8B-class shape, VALU ->
+// matrix unit: 2 rows 78.5-78.8 -> 78.9-79.4 us; 4, 8, 16 and 64 rows 88,
+// 142, 201, 691 -> 80-81, 85, 93-94, 227 us (the VALU kernel reads each
+// activation vector once per row and lane); 0.5B-class at 4 and 16 rows
+// 13.3, 22.7 -> 11.7, 13.5 us.
+constexpr int64_t F32_MFMA_MIN_M = 3;
+
 static int bf16_row_tiles(int64_t M) {
     int64_t mt = ceil_div(M, 16);
     return (int)(mt > 4 ? 4 : (mt < 1 ? 1 : mt));
@@ -483,17 +624,9 @@ static int bf16_pair_blocks(int64_t M, int dt) {
     return (dt == DT_FP8W || M > 8) ? 2 : 1;
 }
 
-// Rows per fp32 workgroup.  Above 8 rows, 16 when the pair blocks alone
-// give at least two workgroups per CU: the weights are then read once per
-// 16 rows instead of 8 (8B-class at 12, 16 and 64 rows 201, 225, 786 ->
-// 171, 201, 691 us with four pieces in flight; eight, 166, 193, 649 us,
-// spill two scalar registers); a smaller matrix keeps 8 and so twice the
-// workgroups (0.5B-class, 304 pair blocks, at 16 rows: 22.5 us, 27.4-29.1
-// with 16).
-static int f32_row_tile(int64_t M, int64_t grid_pb, int num_cus) {
-    if (M > 8 && grid_pb >= 2 * (int64_t)num_cus)
-        return 16;
-    return M >= 8 ? 8 : (M > 2 ? 4 : (M == 2 ? 2 : 1));
+// Rows per workgroup of the fp32 VALU kernel, which serves one and two rows.
+static int f32_row_tile(int64_t M) {
+    return M >= 2 ? 2 : 1;
 }
 
 SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
@@ -503,7 +636,8 @@ SkinnyPlan plan_skinny(const GemmArgs& g, int num_cus)
     p.pb_per_wg = g.dt != DT_F32 ? bf16_pair_blocks(g.M, g.dt) : 1;
     if (g.dt != DT_F32 && g.epi == EPI_PLAIN && g.M > 16)
         p.pb_per_wg = 1;
-    p.row_tile = g.dt != DT_F32 ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M, p.grid_pb, num_cus);
+    const bool f32m = g.dt == DT_F32 && g.M >= F32_MFMA_MIN_M;
+    p.row_tile = (g.dt != DT_F32 || f32m) ? 16 * bf16_row_tiles(g.M) : f32_row_tile(g.M);
     p.row_groups = ceil_div(g.M, p.row_tile);
     // Split K only when there are too few pair blocks (units of weight
     // streaming) to keep every CU busy; two pair blocks per workgroup are
@@ -708,17 +842,39 @@ static void pick_split_f32(const GemmArgs& g, const SkinnyPlan& p, float* partia
 template <int EPI>
 static void pick_rt_f32(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
-    switch (p.row_tile) {
-    case 1: pick_split_f32<1, EPI>(g, p, partial, s); break;
-    case 2: pick_split_f32<2, EPI>(g, p, partial, s); break;
-    case 4: pick_split_f32<4, EPI>(g, p, partial, s); break;
-    case 16:   // four pieces in flight (see f32_row_tile)
-        if (p.splits > 1)
-            go_f32<16, 4, EPI, true>(g, p, partial, s);
-        else
-            go_f32<16, 4, EPI, false>(g, p, partial, s);
-        break;
-    default: pick_split_f32<8, EPI>(g, p, partial, s); break;
+    if (p.row_tile == 1)
+        pick_split_f32<1, EPI>(g, p, partial, s);
+    else
+        pick_split_f32<2, EPI>(g, p, partial, s);
+}
+
+template <int MT, int U, int NPB, int EPI, bool SPLIT, int NWV>
+static void go_f32m(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    dim3 grid((unsigned)ceil_div(p.grid_pb, NPB), (unsigned)p.splits, (unsigned)p.row_groups);
+    skinny_f32m_kernel<MT, U, NPB, EPI, SPLIT, NWV><<<grid, dim3(NWV * 64), 0, s>>>(
+        (const float*)g.a, g.lda, g.geom.K, (const f32x4*)g.w, g.geom.nkc, p.chunks_per_split,
+        (float*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M,
+        (const float*)g.resid, g.ldr, (const float*)g.bias);
+}
+
+template <int MT, int U, int EPI, int NWV>
+static void pick_split_f32m(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    if (p.splits > 1)
+        go_f32m<MT, U, 1, EPI, true, NWV>(g, p, partial, s);
+    else
+        go_f32m<MT, U, 1, EPI, false, NWV>(g, p, partial, s);
+}
+
+template <int EPI>
+static void pick_mt_f32m(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
+{
+    switch (p.row_tile / 16) {
+    case 1: pick_split_f32m<1, 2, EPI, 4>(g, p, partial, s); break;
+    case 2: pick_split_f32m<2, 1, EPI, 8>(g, p, partial, s); break;
+    case 3: pick_split_f32m<3, 1, EPI, 8>(g, p, partial, s); break;
+    default: pick_split_f32m<4, 1, EPI, 8>(g, p, partial, s); break;
     }
 }
 
@@ -767,6 +923,11 @@ hipError_t launch_skinny(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             pick_mt_bf16<EPI_SWIGLU, WF_MXFP4>(g, p, partial, s);
         else
             pick_mt_bf16<EPI_PLAIN, WF_MXFP4>(g, p, partial, s);
+    } else if (g.M >= F32_MFMA_MIN_M) {
+        if (g.epi == EPI_SWIGLU)
+            pick_mt_f32m<EPI_SWIGLU>(g, p, partial, s);
+        else
+            pick_mt_f32m<EPI_PLAIN>(g, p, partial, s);
     } else {
         if (g.epi == EPI_SWIGLU)
             pick_rt_f32<EPI_SWIGLU>(g, p, partial, s);

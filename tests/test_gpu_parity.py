@@ -89,8 +89,9 @@ def test_up_bf16_random(shape, path):
     assert_close(out, ref, BF16, "up bf16 %s path %d" % (shape, path))
 
 
-# the last two take 16-row tiles (at least 512 pair blocks above 8 rows): a
-# partial tile of 12 rows, and 20 rows as one full tile and a partial one
+# from three rows on fp32 takes the matrix-unit kernel: 5, 9 and 33 rows
+# (one, one and three row tiles), and on larger matrices a partial tile of 12
+# rows and 20 rows as one full tile and a partial one
 F32_SHAPES = [(1, 512, 2048), (2, 36, 20), (5, 100, 60), (9, 260, 132), (33, 64, 2048),
               (12, 520, 8200), (20, 264, 8200)]
 

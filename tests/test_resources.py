@@ -23,7 +23,8 @@ B = _build_module()
 
 FAMILIES = ["pack_kernel", "pack_act_kernel", "fp8_scale_kernel", "pack_fp8_kernel",
             "mx_scale_kernel", "pack_mxfp4_kernel", "skinny_bf16_kernel", "skinny_f32_kernel",
-            "splitk_reduce_kernel", "wide_bf16_kernel", "rmsnorm_kernel", "mlp_fused_kernel"]
+            "skinny_f32m_kernel", "splitk_reduce_kernel", "wide_bf16_kernel", "rmsnorm_kernel",
+            "mlp_fused_kernel"]
 
 
 def _record():
