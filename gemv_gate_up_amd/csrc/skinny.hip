@@ -858,23 +858,29 @@ static void go_f32m(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipS
         (const float*)g.resid, g.ldr, (const float*)g.bias);
 }
 
-template <int MT, int U, int EPI, int NWV>
+template <int MT, int U, int NPB, int EPI, int NWV>
 static void pick_split_f32m(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     if (p.splits > 1)
-        go_f32m<MT, U, 1, EPI, true, NWV>(g, p, partial, s);
+        go_f32m<MT, U, NPB, EPI, true, NWV>(g, p, partial, s);
     else
-        go_f32m<MT, U, 1, EPI, false, NWV>(g, p, partial, s);
+        go_f32m<MT, U, NPB, EPI, false, NWV>(g, p, partial, s);
 }
 
+// Two pair blocks per workgroup, so each activation load feeds twice the
+// MFMAs (measured against one: 8B-class at 4, 8, 16 rows 81.5, 86, 93.8 ->
+// 77, 77.7, 81 us with two pieces in flight; at 32 and 64 rows 129, 227 ->
+// 116.7, 195.7 us; 0.5B-class at 16 rows unchanged, at 64 rows 29.5 ->
+// 25.7 us).  The packed buffer holds a multiple of 8 pair blocks, so the
+// second one of the last workgroup is zero padding.
 template <int EPI>
 static void pick_mt_f32m(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
     switch (p.row_tile / 16) {
-    case 1: pick_split_f32m<1, 2, EPI, 4>(g, p, partial, s); break;
-    case 2: pick_split_f32m<2, 1, EPI, 8>(g, p, partial, s); break;
-    case 3: pick_split_f32m<3, 1, EPI, 8>(g, p, partial, s); break;
-    default: pick_split_f32m<4, 1, EPI, 8>(g, p, partial, s); break;
+    case 1: pick_split_f32m<1, 2, 2, EPI, 4>(g, p, partial, s); break;
+    case 2: pick_split_f32m<2, 1, 2, EPI, 8>(g, p, partial, s); break;
+    case 3: pick_split_f32m<3, 1, 2, EPI, 8>(g, p, partial, s); break;
+    default: pick_split_f32m<4, 1, 2, EPI, 8>(g, p, partial, s); break;
     }
 }
 
