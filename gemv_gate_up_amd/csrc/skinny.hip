@@ -720,6 +720,7 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // 4.05, 4.3 us; FP8 at 4 and 8 rows 5.4, 5.6 -> 4.7, 5.0 us; the 8B-
     // and 72B-class shapes unchanged).
     const bool few2 = EPI == EPI_SWIGLU && ceil_div(p.grid_pb, 2) * p.splits < SKINNY_CUS;
+    const bool wide4 = !Q && EPI == EPI_SWIGLU && !few4;   // bf16 gate/up, 17-64 rows (below)
     switch (p.row_tile / 16) {
     case 1:
         if constexpr (WF == WF_MXFP4) {
@@ -814,9 +815,30 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // outweigh the extra trip (8B-class gate/up at 32, 48 and 64 rows 52.4,
     // 56.4, 64.4 -> 46.5, 52.5, 60.8 us; 0.5B-class MLP at 64 rows 22.2 ->
     // 21.4 us)
-    case 2: pick_split_bf16<2, Q ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
-    case 3: pick_split_bf16<3, WF == WF_FP8 ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
-    default: pick_split_bf16<4, WF == WF_FP8 ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s); break;
+    // A bf16 gate/up product of a large matrix takes four pair blocks per
+    // workgroup on four waves: each workgroup reads its whole K range of
+    // the 17-64 activation rows, so four halve those reads against two
+    // (8B-class at 32, 48, 64 rows 45.4, 52.2, 58.8 -> 40.0, 43.9, 48.4 us;
+    // 72B-class at 32 and 64 rows 168, 224 -> 149, 175 us; eight waves
+    // 1-5% slower).  A small one keeps two (the 0.5B-class MLP at 64 rows).
+    case 2:
+        if (wide4)
+            pick_split_bf16<2, 1, 4, EPI, WF, 4>(g, p, partial, s);
+        else
+            pick_split_bf16<2, Q ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s);
+        break;
+    case 3:
+        if (wide4)
+            pick_split_bf16<3, 1, 4, EPI, WF, 4>(g, p, partial, s);
+        else
+            pick_split_bf16<3, WF == WF_FP8 ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s);
+        break;
+    default:
+        if (wide4)
+            pick_split_bf16<4, 1, 4, EPI, WF, 4>(g, p, partial, s);
+        else
+            pick_split_bf16<4, WF == WF_FP8 ? 2 : 1, EPI == EPI_PLAIN ? 1 : 2, EPI, WF, Q ? SK_WAVES : 8>(g, p, partial, s);
+        break;
     }
 }
 
