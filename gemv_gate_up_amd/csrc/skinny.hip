@@ -720,7 +720,7 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // 4.05, 4.3 us; FP8 at 4 and 8 rows 5.4, 5.6 -> 4.7, 5.0 us; the 8B-
     // and 72B-class shapes unchanged).
     const bool few2 = EPI == EPI_SWIGLU && ceil_div(p.grid_pb, 2) * p.splits < SKINNY_CUS;
-    const bool wide4 = !Q && EPI == EPI_SWIGLU && !few4;   // bf16 gate/up, 17-64 rows (below)
+    const bool wide4 = EPI == EPI_SWIGLU && !few4;   // gate/up products at 17-64 rows (below)
     switch (p.row_tile / 16) {
     case 1:
         if constexpr (WF == WF_MXFP4) {
@@ -815,12 +815,15 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // outweigh the extra trip (8B-class gate/up at 32, 48 and 64 rows 52.4,
     // 56.4, 64.4 -> 46.5, 52.5, 60.8 us; 0.5B-class MLP at 64 rows 22.2 ->
     // 21.4 us)
-    // A bf16 gate/up product of a large matrix takes four pair blocks per
-    // workgroup on four waves: each workgroup reads its whole K range of
-    // the 17-64 activation rows, so four halve those reads against two
-    // (8B-class at 32, 48, 64 rows 45.4, 52.2, 58.8 -> 40.0, 43.9, 48.4 us;
-    // 72B-class at 32 and 64 rows 168, 224 -> 149, 175 us; eight waves
-    // 1-5% slower).  A small one keeps two (the 0.5B-class MLP at 64 rows).
+    // A gate/up product of a large matrix takes four pair blocks per
+    // workgroup on four waves, one piece in flight: each workgroup reads its
+    // whole K range of the 17-64 activation rows, so four halve those reads
+    // against two.  bf16: 8B-class at 32, 48, 64 rows 45.4, 52.2, 58.8 ->
+    // 40.0, 43.9, 48.4 us; 72B-class at 32 and 64 rows 168, 224 -> 149, 175
+    // us (eight waves 1-5% slower).  FP8 weights: 8B-class at 32 and 64
+    // rows 32, 48 -> 27.8, 36.7 us, the 72B-class MLP at 32 rows 185 -> 165
+    // us; MXFP4: 27, 41 -> 21.6, 32 us, the 72B-class MLP at 64 rows 264 ->
+    // 222 us.  A small one keeps two (the 0.5B-class MLP at 64 rows).
     case 2:
         if (wide4)
             pick_split_bf16<2, 1, 4, EPI, WF, 4>(g, p, partial, s);
