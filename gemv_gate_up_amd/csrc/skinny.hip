@@ -7,10 +7,10 @@
 // activations the grid is cut along the weights, which are large, not along
 // the output, which is small.  Each workgroup owns one to four consecutive
 // pair blocks of the packed weights (16 gate + 16 up columns, or 32 down
-// columns, each) and a range of K; its four waves take interleaved K
-// pieces, each lane streaming 16-byte nontemporal loads with several in
-// flight.  Partial sums of the
-// waves are combined in LDS in a fixed order.  When the pair blocks alone
+// columns, each) and a range of K; its four or eight waves take
+// interleaved K pieces, each lane streaming 16-byte nontemporal loads with
+// several in flight.  Partial sums of the waves are combined in LDS in a
+// fixed order.  When the pair blocks alone
 // do not fill the GPU, K is also split across workgroups and a second pass
 // adds the slices in ascending order; no atomics are used, so results are
 // reproducible run to run (same section: the authors reject an atomic add
@@ -22,7 +22,8 @@
 // bf16 weights are multiplied on v_mfma_f32_16x16x32_bf16 with the
 // activations as the 16-row A operand: at M <= 16 the matrix unit has spare
 // throughput, and above M = 4 plain fp32 FMA on the VALU would take longer
-// than streaming the weights.  fp32 weights use VALU FMA.
+// than streaming the weights.  fp32 weights use VALU FMA at one and two
+// rows and v_mfma_f32_16x16x4_f32 from three rows on.
 //
 // FP8 weights (WF = WF_FP8) halve the streamed bytes: each 16-byte load
 // brings 16 E4M3 codes that widen exactly to bf16 (every E4M3 value is a
