@@ -422,10 +422,15 @@ skinny_f32m_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
 }
 
 // ---------------------------------------------------------------- fp32 (VALU)
-// Lane l covers column l % 16 and k-group l / 16 (4 consecutive K values)
-// of each piece; the four k-groups are added with two butterfly steps whose
-// result is the same in every lane, then the waves are added in LDS.
-template <int RT, int U, int EPI, bool SPLIT, typename OutT>
+// A workgroup covers 16 / CS columns of each half of one pair block (CS
+// workgroups share a pair block; CS > 1 only without a split of K).  Lane l
+// covers column l % CW of that share, k-group (l / CW) % 4 (4 consecutive K
+// values) and piece CS * v + l / (4 CW) of its step v, so every lane's
+// 16-byte load is useful; the lanes of a column are added with butterfly
+// steps whose result is the same in each of them, then the waves are added
+// in LDS.  With CS = 1 a lane covers column l % 16 and k-group l / 16 of
+// every piece.
+template <int RT, int U, int EPI, bool SPLIT, typename OutT, int CS = 1>
 __global__ void __launch_bounds__(SK_THREADS)
 skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
                   const f32x4* __restrict__ w, int64_t nkc, int64_t cps,
@@ -433,15 +438,20 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
                   float* __restrict__ partial, int64_t npc, int M,
                   const OutT* __restrict__ resid, int64_t ldr, const OutT* __restrict__ bias)
 {
+    static_assert(CS == 1 || (CS == 2 || CS == 4) && !SPLIT, "column shares without a K split");
+    constexpr int CW = 16 / CS;   // columns of each half per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t pb = blockIdx.x;
+    const int64_t pb = blockIdx.x / CS;
+    const int cbase = (int)(blockIdx.x % CS) * CW;
     const int s = blockIdx.y;
     const int rbase = blockIdx.z * RT;
     const int64_t kbeg = (int64_t)s * cps;
     const int64_t kend = kbeg + cps < nkc ? kbeg + cps : nkc;
-    const f32x4* wp = w + pb * nkc * 2 * PIECE_VECS + lane;
-    const int koff = (lane >> 4) * 4;
+    const int lp = lane / (4 * CW);   // piece of the lane within a step's CS pieces
+    const int kgrp = (lane / CW) % 4;
+    const f32x4* wp = w + pb * nkc * 2 * PIECE_VECS + kgrp * 16 + cbase + lane % CW;
+    const int koff = kgrp * 4;
 
     float accg[RT], accu[RT];
 #pragma unroll
@@ -450,11 +460,13 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
         accu[r] = 0.f;
     }
 
-    for (int64_t kb = kbeg + wave; kb < kend; kb += SK_WAVES * U) {
+    // step v of the loop covers pieces kbeg + CS * v .. + CS - 1
+    const int64_t nv = (kend - kbeg + CS - 1) / CS;
+    for (int64_t vb = wave; vb < nv; vb += SK_WAVES * U) {
         f32x4 wg[U], wu[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t kc = kb + SK_WAVES * u;
+            const int64_t kc = kbeg + (vb + SK_WAVES * u) * CS + lp;
             if (kc < kend) {
                 wg[u] = __builtin_nontemporal_load(wp + (kc * 2) * PIECE_VECS);
                 wu[u] = __builtin_nontemporal_load(wp + (kc * 2 + 1) * PIECE_VECS);
@@ -474,7 +486,7 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
             f32x4 xv[XB][RT];
 #pragma unroll
             for (int i = 0; i < XB; ++i) {
-                const int64_t kc = kb + SK_WAVES * (u0 + i);
+                const int64_t kc = kbeg + (vb + SK_WAVES * (u0 + i)) * CS + lp;
                 const int64_t k = kc * 16 + koff;
 #pragma unroll
                 for (int r = 0; r < RT; ++r) {
@@ -503,13 +515,14 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
 
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-        accg[r] += __shfl_xor(accg[r], 16);
-        accg[r] += __shfl_xor(accg[r], 32);
-        accu[r] += __shfl_xor(accu[r], 16);
-        accu[r] += __shfl_xor(accu[r], 32);
+#pragma unroll
+        for (int m = CW; m < 64; m *= 2) {
+            accg[r] += __shfl_xor(accg[r], m);
+            accu[r] += __shfl_xor(accu[r], m);
+        }
     }
-    __shared__ float red[SK_WAVES][2][RT][16];
-    if (lane < 16) {
+    __shared__ float red[SK_WAVES][2][RT][CW];
+    if (lane < CW) {
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             red[wave][0][r][lane] = accg[r];
@@ -518,14 +531,14 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
     }
     __syncthreads();
     const int t = threadIdx.x;
-    if (t >= RT * 16)
+    if (t >= RT * CW)
         return;
-    const int r = t >> 4, c = t & 15;
+    const int r = t / CW, c = cbase + t % CW;
     float g = 0.f, u = 0.f;
 #pragma unroll
     for (int wv = 0; wv < SK_WAVES; ++wv) {
-        g += red[wv][0][r][c];
-        u += red[wv][1][r][c];
+        g += red[wv][0][r][t % CW];
+        u += red[wv][1][r][t % CW];
     }
     const int row = rbase + r;
     if (row >= M)
@@ -846,11 +859,19 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     }
 }
 
-template <int RT, int U, int EPI, bool SPLIT>
+// Workgroups per pair block of the fp32 VALU kernel when the pair blocks
+// alone would leave at least half the CUs without a workgroup (no K split):
+// two, each lane group still reading whole 128-byte lines (512 x 2048 at
+// one row 4.18 -> 4.03-4.28 us, at two rows 4.62 -> 4.42-4.47 us, its MLP
+// 9.95 -> 9.85 us); four, with 64-byte segments, were slower (5.5, 6.0,
+// 11.0 us).
+constexpr int F32_COL_SHARES = 2;
+
+template <int RT, int U, int EPI, bool SPLIT, int CS = 1>
 static void go_f32(const GemmArgs& g, const SkinnyPlan& p, float* partial, hipStream_t s)
 {
-    dim3 grid((unsigned)p.grid_pb, (unsigned)p.splits, (unsigned)p.row_groups);
-    skinny_f32_kernel<RT, U, EPI, SPLIT, float><<<grid, dim3(SK_THREADS), 0, s>>>(
+    dim3 grid((unsigned)(p.grid_pb * CS), (unsigned)p.splits, (unsigned)p.row_groups);
+    skinny_f32_kernel<RT, U, EPI, SPLIT, float, CS><<<grid, dim3(SK_THREADS), 0, s>>>(
         (const float*)g.a, g.lda, g.geom.K, (const f32x4*)g.w, g.geom.nkc, p.chunks_per_split,
         (float*)g.out, g.ldo, g.ncols_out, partial, g.geom.npb * 32, (int)g.M,
         (const float*)g.resid, g.ldr, (const float*)g.bias);
@@ -861,6 +882,8 @@ static void pick_split_f32(const GemmArgs& g, const SkinnyPlan& p, float* partia
 {
     if (p.splits > 1)
         go_f32<RT, 8, EPI, true>(g, p, partial, s);
+    else if (p.grid_pb * p.row_groups * 2 <= SKINNY_CUS)
+        go_f32<RT, 8, EPI, false, F32_COL_SHARES>(g, p, partial, s);
     else
         go_f32<RT, 8, EPI, false>(g, p, partial, s);
 }

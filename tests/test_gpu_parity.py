@@ -95,9 +95,11 @@ def test_up_bf16_random(shape, path):
 
 # from three rows on fp32 takes the matrix-unit kernel: 5, 9 and 33 rows
 # (one, one and three row tiles), and on larger matrices a partial tile of 12
-# rows and 20 rows as one full tile and a partial one
+# rows and 20 rows as one full tile and a partial one; up to two rows, a
+# product of fewer pair blocks than half the CUs shares each pair block
+# between workgroups (1 x 512 x 2048, 2 x 36 x 20, 2 x 264 x 1000)
 F32_SHAPES = [(1, 512, 2048), (2, 36, 20), (5, 100, 60), (9, 260, 132), (33, 64, 2048),
-              (12, 520, 8200), (20, 264, 8200)]
+              (12, 520, 8200), (20, 264, 8200), (2, 264, 1000)]
 
 
 @pytest.mark.parametrize("shape", F32_SHAPES)
@@ -113,7 +115,7 @@ def test_up_f32_random(shape):
 
 MLP_SHAPES = [(1, 256, 512, BF16), (7, 136, 392, BF16), (64, 896, 4864, BF16),
               (130, 264, 712, BF16), (4, 100, 60, F32), (12, 64, 520, F32),
-              (20, 264, 8200, F32)]
+              (20, 264, 8200, F32), (1, 200, 1000, F32), (2, 600, 100, F32)]
 
 
 @pytest.mark.parametrize("shape", MLP_SHAPES)
