@@ -92,8 +92,10 @@ skinny_bf16_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t kvalid,
     // it was measured faster: 8B-class decode at 1, 4, 8 and 16 rows
     // 37.45, 38.3, 39.2, 38.4 -> 37.3, 37.8, 38.6, 37.6 us (with the pieces
     // in flight re-tuned for it in pick_mt_bf16); slower with FP8 or MXFP4
-    // weights (8B decode at 16 rows 23.6 -> 25.4 us and 15.6 -> 16.2 us)
-    // and with four row tiles (0.5B-class MLP at 64 rows 19.8 -> 20.0 us).
+    // weights (8B decode at 16 rows 23.6 -> 25.4 us and 15.6 -> 16.2 us, at
+    // one row 20.8 -> 21.7 us and 13.1 -> 14.7 us, also with two pieces in
+    // flight) and with four row tiles (0.5B-class MLP at 64 rows 19.8 ->
+    // 20.0 us).
     constexpr bool PIPE = WF == WF_BF16 && MT == 1;
     const float* colscale = (const float*)scales;                       // FP8: per column
     const int lane = threadIdx.x & 63;
