@@ -984,6 +984,12 @@ def summarize(d: str) -> int:
             "stream around the same steps): %.2f us per step, roofline frac %.4f of %s %s." % (
                 ksum, span / 1e3, rl["event_ms_per_step"] * 1e3, rl["frac"], rl["peak"],
                 rl["unit"]),
+        ] + ([
+            "",
+            "In this traced run the span and the events include gaps between the launches that "
+            "the tracer adds (%.2f us per step beyond the kernels' own time); the kernel "
+            "averages are the figures to compare with an untraced run's events." % (
+                span / 1e3 - ksum)] if span / 1e3 > 1.1 * ksum else []) + [
             "",
             "HBM traffic per step: fetch %d B + write %d B = **%d B** against %d algorithmic "
             "bytes (ratio %.2f)." % (sum(fb), sum(wb), total, alg, total / alg)]
