@@ -7,12 +7,12 @@
 // activations the grid is cut along the weights, which are large, not along
 // the output, which is small.  Each workgroup owns one to four consecutive
 // pair blocks of the packed weights (16 gate + 16 up columns, or 32 down
-// columns, each) and a range of K; its four or eight waves take
-// interleaved K pieces, each lane streaming 16-byte nontemporal loads with
-// several in flight.  Partial sums of the waves are combined in LDS in a
-// fixed order.  When the pair blocks alone
-// do not fill the GPU, K is also split across workgroups and a second pass
-// adds the slices in ascending order; no atomics are used, so results are
+// columns, each; the fp32 one- and two-row kernel can own half of one) and a
+// range of K; its four or eight waves take interleaved K pieces, each lane
+// streaming 16-byte nontemporal loads with several in flight.  Partial sums
+// of the waves are combined in LDS in a fixed order.  When the pair blocks
+// alone do not fill the GPU, K is also split across workgroups and a second
+// pass adds the slices in ascending order; no atomics are used, so results are
 // reproducible run to run (same section: the authors reject an atomic add
 // into the output for that reason).  silu(g) * u is applied once the full
 // K sum is known (the second pass or the LDS combine), like the bias of the
@@ -440,7 +440,7 @@ skinny_f32_kernel(const float* __restrict__ a, int64_t lda, int64_t kvalid,
                   float* __restrict__ partial, int64_t npc, int M,
                   const OutT* __restrict__ resid, int64_t ldr, const OutT* __restrict__ bias)
 {
-    static_assert(CS == 1 || (CS == 2 || CS == 4) && !SPLIT, "column shares without a K split");
+    static_assert(CS == 1 || ((CS == 2 || CS == 4) && !SPLIT), "column shares without a K split");
     constexpr int CW = 16 / CS;   // columns of each half per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
