@@ -112,3 +112,54 @@ def test_the_rule_splits_where_blocks_are_few():
     assert _slices(1, 512, 2048, 16, F32, True)[0] == 1
     assert _slices(64, 4864, 896, 32, BF16, False)[0] == 8
     assert _slices(64, 896, 4864, 16, BF16, True)[0] == 1
+
+
+# ---------------------------------------------------------------- dispatcher
+# The automatic path of a gate/up product (swiglu_select_path): bf16 above
+# 64 rows takes the wide MFMA kernel when its grid keeps the chip busy, and
+# every other product the few-rows kernels.  The wide grid counts 256 x 256
+# tiles (8 pair blocks of 16 gate + 16 up columns across); a grid of at most
+# 128 of them runs as narrower tiles instead, 128 x 128 up to 128 rows and
+# 256 x 128 above, and the dispatcher counts those.  Wide when that count is
+# at least 128, or at least 48 from 256 rows on.
+
+def _wide_tiles(M, dff):
+    pbs = _cdiv(dff, 16)
+    full = _cdiv(M, 256) * _cdiv(pbs, 8)
+    if full > CUS // 2:
+        return full
+    return _cdiv(M, 128 if M <= 128 else 256) * _cdiv(pbs, 4)
+
+
+def _auto_path(M, d, dff, dt):
+    if dt == BF16 and M > 64:
+        t = _wide_tiles(M, dff)
+        if t >= CUS // 2 or (M >= 256 and t >= 48):
+            return sw.SWIGLU_PATH_WIDE
+    return SKINNY
+
+
+@pytest.mark.parametrize("dt", [BF16, F32, W8, W4])
+def test_automatic_path_follows_the_grid_rule(dt):
+    bad = []
+    for M, d, dff in itertools.product(
+            [1, 16, 64, 65, 96, 128, 129, 192, 255, 256, 300, 512, 1024, 4096],
+            [896, 1536, 4096, 8192], [896, 3696, 4864, 8960, 14336, 29568]):
+        got = sw.swiglu_select_path(M, d, dff, dt)
+        if got != _auto_path(M, d, dff, dt):
+            bad.append(((M, d, dff), got))
+    assert not bad, bad[:10]
+
+
+def test_the_grid_rule_on_named_shapes():
+    # the 8B prefill and the 72B MLP's products are wide; the 0.5B-class
+    # gate/up product (76 narrow tiles from 129 to 256 rows) stays on the
+    # few-rows kernels below 256 rows and goes wide at 256; the 8B shape
+    # takes the wide kernel from 65 rows (224 narrow tiles)
+    assert _auto_path(4096, 4096, 14336, BF16) == sw.SWIGLU_PATH_WIDE
+    assert _auto_path(2048, 8192, 29568, BF16) == sw.SWIGLU_PATH_WIDE
+    assert _wide_tiles(255, 4864) == _wide_tiles(256, 4864) == 76
+    assert _auto_path(255, 896, 4864, BF16) == SKINNY
+    assert _auto_path(256, 896, 4864, BF16) == sw.SWIGLU_PATH_WIDE
+    assert _auto_path(65, 4096, 14336, BF16) == sw.SWIGLU_PATH_WIDE
+    assert _wide_tiles(65, 14336) == 224
