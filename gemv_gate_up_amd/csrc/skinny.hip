@@ -723,13 +723,26 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // MXFP4 activation fragments (4 per piece and row tile) bound U above
     // two row tiles
     constexpr bool Q = WF != WF_BF16;
-    // Four pair blocks per workgroup leave a small gate/up product (the
-    // 0.5B-class shape: 304 pair blocks, 76 workgroups) on under half the
-    // CUs; such products take two per workgroup above 8 rows (0.5B-class
-    // at 16 rows: bf16 9.0 -> 6.5 us, its MLP 16.7 -> 14.1 us; FP8 weights
-    // 7.2 -> 5.3 us, MXFP4 6.1 -> 4.7 us; the 8B-class shape and the
-    // 72B-class tensor-parallel shard, 224 and 232 workgroups, keep four).
-    const bool few4 = EPI == EPI_SWIGLU && ceil_div(p.grid_pb, 4) * p.splits < SKINNY_CUS / 2;
+    // Above 8 rows a gate/up product takes four pair blocks per workgroup
+    // (one activation fragment feeds more weights) unless two leave the
+    // busiest CU less to stream: its workgroups times each one's bytes,
+    // counted in quarters of a bf16 pair block (a bf16 pair block 4, FP8
+    // 2, MXFP4 1; one 16-row activation tile over the same K 2).  A small
+    // product takes two (the 0.5B-class shape, 304 pair blocks: at 16 rows
+    // bf16 9.0 -> 6.5 us, its MLP 16.7 -> 14.1 us, FP8 7.2 -> 5.3 us, MXFP4
+    // 6.1 -> 4.7 us), and so does one whose four-block grid would leave a
+    // few CUs with a second workgroup or half of them idle (7B-class 3584 x
+    // 18944 at 16 rows, 296 workgroups: bf16 56.5 -> 48.9 us, FP8 31.9 ->
+    // 28.9 us; 3B-class 3072 x 8192, 128 workgroups: 16 rows bf16 23.3 ->
+    // 18.8 us, MXFP4 11.4 -> 8.6 us, 64 rows bf16 35.1 -> 26.9 us; 1B-class
+    // 2048 x 8192 at 16 rows 16.7 -> 13.5 us).  The 8B- and 72B-class
+    // shapes keep four.
+    const int64_t wq = WF == WF_BF16 ? 4 : (WF == WF_FP8 ? 2 : 1);
+    const int64_t xq = 2 * (p.row_tile / 16);
+    auto cu_load = [&](int64_t n) {
+        return ceil_div(ceil_div(p.grid_pb, n) * p.splits, SKINNY_CUS) * (wq * n + xq);
+    };
+    const bool few4 = EPI == EPI_SWIGLU && cu_load(4) > cu_load(2);
     // Likewise up to 8 rows with FP8 and MXFP4 weights: where two pair
     // blocks per workgroup would give fewer workgroups than CUs, one (the
     // 0.5B-class shape at 1, 4 and 8 rows: MXFP4 4.1, 4.2, 4.7 -> 3.9,
@@ -751,7 +764,7 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
             // workgroup reads as many activation bytes as it has K, so the
             // smaller gate/up products also take four pair blocks per wave,
             // on eight waves (8B-class at 16 rows 15.8 -> 15.5 us)
-            if (g.M > 8 && p.grid_pb >= 4 * MXFP4_WIDE_PB_CUS)
+            if (g.M > 8 && !few4 && p.grid_pb >= 4 * MXFP4_WIDE_PB_CUS)
                 pick_split_bf16<1, 1, 4, EPI, WF>(g, p, partial, s);
             else if (g.M > 8 && few4)
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);

@@ -71,9 +71,10 @@ def test_pack_matches_the_oracle_quantiser_bitwise(d, dff):
     assert np.array_equal(sd[:d].view(np.uint32), rs.view(np.uint32))
 
 
-# (40, 520, 8200): four pair blocks per workgroup at 17-64 rows, ragged tail
+# (40, 520, 8200): four pair blocks per workgroup at 17-64 rows, ragged tail;
+# (16, 264, 18944): 1,184 pair blocks, two per workgroup for balance
 UP_SHAPES = [(1, 512, 2048), (3, 264, 200), (16, 1032, 776), (17, 520, 1048), (40, 136, 3000),
-             (64, 896, 4864), (100, 328, 1000), (40, 520, 8200)]
+             (64, 896, 4864), (100, 328, 1000), (40, 520, 8200), (16, 264, 18944)]
 
 
 def _quantised(inp):

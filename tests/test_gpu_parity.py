@@ -71,13 +71,14 @@ def test_pack_roundtrip_bitwise(dtype, d, dff):
 
 # ---------------------------------------------------------------- random parity
 # (M, d, dff): tile-spanning shapes with ragged tails in M, d (K) and dff (N).
-# The last three have at least 512 pair blocks at 17-64 rows, where the
-# skinny path takes four pair blocks per workgroup (two, three and four row
-# tiles).
+# Three have at least 512 pair blocks at 17-64 rows, where the skinny path
+# takes four pair blocks per workgroup (two, three and four row tiles); the
+# last has 1,184 pair blocks at 16 rows, where two per workgroup balance the
+# CUs better than four.
 BF16_UP_SHAPES = [
     (1, 512, 2048), (3, 264, 200), (16, 1032, 776), (17, 520, 1048), (40, 136, 3000),
     (64, 896, 4864), (65, 256, 264), (100, 328, 1000), (300, 1000, 1400), (513, 64, 512),
-    (20, 264, 8200), (40, 520, 8200), (64, 1032, 8200),
+    (20, 264, 8200), (40, 520, 8200), (64, 1032, 8200), (16, 264, 18944),
 ]
 
 
