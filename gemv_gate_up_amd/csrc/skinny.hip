@@ -749,6 +749,15 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
     // 4.05, 4.3 us; FP8 at 4 and 8 rows 5.4, 5.6 -> 4.7, 5.0 us; the 8B-
     // and 72B-class shapes unchanged).
     const bool few2 = EPI == EPI_SWIGLU && ceil_div(p.grid_pb, 2) * p.splits < SKINNY_CUS;
+    // Where two pair blocks per workgroup give exactly one workgroup per CU
+    // (512 pair blocks: d_ff = 8192), FP8 and MXFP4 gate/up products of 3
+    // to 8 rows run them on eight waves, one piece per half in flight: four
+    // waves would leave one wave per SIMD with nothing to hide its loads
+    // behind (3B-class 3072 x 8192: FP8 at 4 and 8 rows 12.8, 13.35 ->
+    // 10.2, 10.95 us, MXFP4 at 8 rows 10.0 -> 8.2 us; with more than one
+    // workgroup per CU four waves stay faster: 8B-, 13B- and 72B-class FP8
+    // at 8 rows 2-5% slower on eight).
+    const bool one2 = EPI == EPI_SWIGLU && ceil_div(p.grid_pb, 2) * p.splits <= SKINNY_CUS;
     const bool wide4 = EPI == EPI_SWIGLU && !few4;   // gate/up products at 17-64 rows (below)
     switch (p.row_tile / 16) {
     case 1:
@@ -776,6 +785,8 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
                 pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else if (few2)
                 pick_split_bf16<1, 1, 1, EPI, WF, 8>(g, p, partial, s);
+            else if (one2)
+                pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else
                 pick_split_bf16<1, 1, 2, EPI, WF>(g, p, partial, s);
         } else if constexpr (Q) {
@@ -801,6 +812,8 @@ static void pick_mt_bf16(const GemmArgs& g, const SkinnyPlan& p, float* partial,
                 pick_split_bf16<1, 1, 4, EPI, WF, 8>(g, p, partial, s);
             else if (few2)
                 pick_split_bf16<1, 2, 1, EPI, WF, 8>(g, p, partial, s);
+            else if (one2)
+                pick_split_bf16<1, 1, 2, EPI, WF, 8>(g, p, partial, s);
             else
                 pick_split_bf16<1, 2, 2, EPI, WF>(g, p, partial, s);
         } else {

@@ -72,9 +72,10 @@ def test_pack_matches_the_oracle_quantiser_bitwise(d, dff):
 
 
 # (40, 520, 8200): four pair blocks per workgroup at 17-64 rows, ragged tail;
-# (16, 264, 18944): 1,184 pair blocks, two per workgroup for balance
+# (16, 264, 18944): 1,184 pair blocks, two per workgroup for balance;
+# (5, 264, 8192): 512 pair blocks, one workgroup per CU on eight waves
 UP_SHAPES = [(1, 512, 2048), (3, 264, 200), (16, 1032, 776), (17, 520, 1048), (40, 136, 3000),
-             (64, 896, 4864), (100, 328, 1000), (40, 520, 8200), (16, 264, 18944)]
+             (64, 896, 4864), (100, 328, 1000), (40, 520, 8200), (16, 264, 18944), (5, 264, 8192)]
 
 
 def _quantised(inp):

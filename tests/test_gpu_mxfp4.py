@@ -72,10 +72,12 @@ def _deq(inp):
             for k in ("wg", "wu", "wd") if k in inp}
 
 
-# the last two: four pair blocks per workgroup at 17-64 rows, ragged tail
+# (40, 520, 8200) and (64, 1032, 8200): four pair blocks per workgroup at
+# 17-64 rows, ragged tail; (6, 264, 8192): one workgroup per CU on eight waves
 @pytest.mark.parametrize("shape", [(1, 512, 2048), (3, 264, 200), (16, 1032, 776),
                                    (17, 520, 1048), (40, 136, 3000), (64, 896, 4864),
-                                   (100, 328, 1000), (40, 520, 8200), (64, 1032, 8200)])
+                                   (100, 328, 1000), (40, 520, 8200), (64, 1032, 8200),
+                                   (6, 264, 8192)])
 def test_up_mxfp4_random(shape):
     M, d, dff = shape
     say("up mxfp4", shape)
